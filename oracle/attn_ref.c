@@ -1,0 +1,197 @@
+/*
+ * FP64 reference attention -- TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the oracle against which the GPU attention library is checked.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load it.  It shares no code, header or constant with the GPU library.
+ *
+ * What it computes is the plain definition of scaled-dot-product attention
+ * as given on the page "Ch.04 Attention optimisation: FlashAttention and
+ * sparse attention" (mdooai.com), sections "Core formula" and "Key points of
+ * the formulas":
+ *
+ *     S_ij = scale * (q_i . k_j)           (scale = 1/sqrt(d_k) by default)
+ *     A_i: = softmax_j(S_i:),  sum_j A_ij = 1
+ *     O_i  = sum_j A_ij v_j                (O = A V)
+ *
+ * and the same page's sparse-attention rule: for a key j outside the allowed
+ * set of query i the logit is set to -infinity before the softmax, so A_ij = 0.
+ * The FlashAttention summary page ("FlashAttention: Fast and Memory-Efficient
+ * Exact Attention with IO-Awareness", ai-paper-library, Summary and Method)
+ * states the tiled method is exact, i.e. it reaches this same result; the
+ * oracle is therefore the definition itself, written out with S (and A, in
+ * place) materialised, with no tiling and no online softmax.
+ *
+ * Allowed-set readings where the pages are silent:
+ *   causal      : key j allowed for query i iff j <= i
+ *   key padding : key j allowed iff j < key_len[b]
+ *   block mask  : key j allowed iff mask[(i / blk) * nkb + (j / blk)] != 0,
+ *                 nkb = ceil(N / blk); the mask is shared by every (b, h)
+ *   a row with no allowed key gets O_i = 0 and LSE_i = -infinity.
+ * The row maximum is subtracted before exp (a rewrite that leaves the softmax
+ * unchanged) so that large logits do not overflow.
+ * LSE_i = log(sum_j exp(S_ij)) in natural log.
+ *
+ * Layout: q, k, v, o are contiguous [B, H, N, d]; lse is [B, H, N].
+ * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/build.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+static int key_allowed(int64_t i, int64_t j, int64_t b, int causal,
+                       const int32_t *key_len, const uint8_t *block_mask,
+                       int64_t blk, int64_t nkb)
+{
+    if (causal && j > i) return 0;
+    if (key_len && j >= (int64_t)key_len[b]) return 0;
+    if (block_mask && block_mask[(i / blk) * nkb + (j / blk)] == 0) return 0;
+    return 1;
+}
+
+/* Softmax of one materialised row s[0..N) in place (s becomes the row of A),
+ * then o = A_row V and the row's logsumexp.  Returns nothing; a row whose
+ * logits are all -inf gives o = 0, lse = -inf. */
+static void softmax_row_times_v(double *s, const double *vh, double *o,
+                                double *lse, int64_t N, int64_t d)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < N; ++j)
+        if (s[j] > m) m = s[j];
+    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+    if (m == -INFINITY) {
+        for (int64_t j = 0; j < N; ++j) s[j] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+        s[j] = exp(s[j] - m); /* exp(-inf) = 0 for masked keys */
+        l += s[j];
+    }
+    for (int64_t j = 0; j < N; ++j) s[j] /= l;
+    for (int64_t j = 0; j < N; ++j) {
+        if (s[j] == 0.0) continue;
+        const double *vj = vh + j * d;
+        for (int64_t c = 0; c < d; ++c) o[c] += s[j] * vj[c];
+    }
+    *lse = m + log(l);
+}
+
+static void score_row(double *s, const double *qi, const double *kh, int64_t i,
+                      int64_t b, int64_t N, int64_t d, double scale, int causal,
+                      const int32_t *key_len, const uint8_t *block_mask,
+                      int64_t blk, int64_t nkb)
+{
+    for (int64_t j = 0; j < N; ++j) {
+        if (!key_allowed(i, j, b, causal, key_len, block_mask, blk, nkb)) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        const double *kj = kh + j * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+        s[j] = scale * dot;
+    }
+}
+
+static int check_args(const double *q, const double *k, const double *v,
+                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      const uint8_t *block_mask, int64_t blk)
+{
+    if (!q || !k || !v) return 1;
+    if (B < 0 || H < 0 || N < 0 || d <= 0) return 2;
+    if (block_mask && blk <= 0) return 2;
+    return 0;
+}
+
+/* Full evaluation: every (b, h) head, S materialised as an N x N array of
+ * doubles one head at a time (A overwrites S in place).  Returns 0 on success,
+ * non-zero on bad arguments or allocation failure. */
+int attn_ref_f64(const double *q, const double *k, const double *v, double *o,
+                 double *lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                 double scale, int causal, const int32_t *key_len,
+                 const uint8_t *block_mask, int64_t blk)
+{
+    int rc = check_args(q, k, v, B, H, N, d, block_mask, blk);
+    if (rc) return rc;
+    if (!o || !lse) return 1;
+    if (N == 0) return 0;
+    const int64_t nkb = block_mask ? (N + blk - 1) / blk : 0;
+    double *S = (double *)malloc((size_t)N * (size_t)N * sizeof(double));
+    if (!S) return 3;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t head = (b * H + h) * N;
+            const double *qh = q + head * d, *kh = k + head * d, *vh = v + head * d;
+            double *oh = o + head * d, *lh = lse + head;
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t i = 0; i < N; ++i)
+                score_row(S + i * N, qh + i * d, kh, i, b, N, d, scale, causal,
+                          key_len, block_mask, blk, nkb);
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t i = 0; i < N; ++i)
+                softmax_row_times_v(S + i * N, vh, oh + i * d, lh + i, N, d);
+        }
+    }
+    free(S);
+    return 0;
+}
+
+/* Sampled evaluation: only the query rows listed in rows[] are computed.
+ * rows[r] is a flat row index (b * H + h) * N + i.  o_rows is [n_rows, d],
+ * lse_rows is [n_rows].  Each row is the same definition as above, with that
+ * row of S materialised on its own. */
+int attn_ref_rows_f64(const double *q, const double *k, const double *v,
+                      int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                      int causal, const int32_t *key_len,
+                      const uint8_t *block_mask, int64_t blk,
+                      const int64_t *rows, int64_t n_rows, double *o_rows,
+                      double *lse_rows)
+{
+    int rc = check_args(q, k, v, B, H, N, d, block_mask, blk);
+    if (rc) return rc;
+    if (n_rows > 0 && (!rows || !o_rows || !lse_rows)) return 1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * H * N) return 2;
+    if (n_rows == 0) return 0;
+    const int64_t nkb = block_mask ? (N + blk - 1) / blk : 0;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (!s) continue;
+            const int64_t flat = rows[r];
+            const int64_t head = flat / N, i = flat % N, b = head / H;
+            const double *kh = k + head * N * d, *vh = v + head * N * d;
+            score_row(s, q + flat * d, kh, i, b, N, d, scale, causal, key_len,
+                      block_mask, blk, nkb);
+            softmax_row_times_v(s, vh, o_rows + r * d, lse_rows + r, N, d);
+        }
+        free(s);
+    }
+    return failed ? 3 : 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (for reporting). */
+int attn_ref_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
