@@ -1,0 +1,132 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The library computes, for every batch entry b and head h,
+ *
+ *     S   = scale * Q K^T                      (N x N, never stored)
+ *     A   = row-softmax(S), disallowed keys at -inf before the softmax
+ *     O   = A V
+ *     LSE = log(sum_j exp(S_ij)) over the allowed keys j   (natural log)
+ *
+ * which is scaled-dot-product attention as defined on the page "Ch.04
+ * Attention optimisation: FlashAttention and sparse attention" (mdooai.com,
+ * sections "Core formula" and "Key points of the formulas", including the
+ * -inf masking rule of its sparse-attention paragraph).  It is computed tile
+ * by tile with a running row maximum and running row sum, so S and A never
+ * reach device memory: the IO-aware exact method summarised on the page
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with
+ * IO-Awareness" (ai-paper-library, Summary and Method), including its
+ * block-sparse extension, and the five-stage map (tile Q/K/V, stage blocks on
+ * chip, local scores with running normalisation, accumulate without the full
+ * matrix, schedule for the accelerator) on the page "What is FlashAttention?"
+ * (unite.ai, "Five-stage operating map").
+ *
+ * Allowed set of key j for query i (all conditions must hold):
+ *   causal != 0        : j <= i
+ *   key_len != NULL    : j < key_len[b]   (value clamped to [0, N])
+ *   block_mask != NULL : block_mask[(i/128) * nb + (j/128)] != 0,
+ *                        nb = ceil(N/128); one mask shared by every (b, h)
+ * A query row with no allowed key gets O = 0 and LSE = -inf.
+ *
+ * Layout and ownership (every entry point):
+ *   q, k, v, o : DEVICE pointers, contiguous [B, H, N, d], d innermost,
+ *                16-byte aligned; owned by the caller.  o must not overlap
+ *                q, k or v.
+ *   lse        : DEVICE pointer to float [B, H, N] (4-byte aligned) or NULL
+ *                (then no logsumexp is written).
+ *   key_len    : DEVICE pointer to int32 [B] or NULL.
+ *   block_mask : DEVICE pointer to uint8 [nb * nb] or NULL; row = query
+ *                block, column = key block, 128 x 128 tokens per block.
+ *   scale      : the softmax scale (1/sqrt(d) for standard attention); any
+ *                finite value.
+ *   stream     : HIP stream the work is enqueued on (NULL = default stream).
+ *   B, H, N    : >= 1, with B*H*ceil(N/16) < 2^31.
+ *   d          : 64 or 128.
+ *
+ * Behaviour: each call validates its arguments on the host and returns a
+ * status code before making any HIP call; on success the work is enqueued
+ * asynchronously on `stream` (the call never synchronises and never
+ * allocates device or host memory).  A failed launch returns FA_ERR_HIP and
+ * the hipError_t is kept for fa_last_hip_error() on the calling thread.  The
+ * library never prints or aborts.  Results are deterministic: no atomics,
+ * identical bits from run to run for the same inputs and tile choice.
+ * Non-finite inputs propagate unchecked.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL_PTR = 1,             /* q, k, v or o is NULL                        */
+    FA_ERR_INVALID_SHAPE = 2,        /* B, H or N < 1, or the grid would overflow   */
+    FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128}                          */
+    FA_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte, lse/key_len not 4-byte */
+    FA_ERR_UNSUPPORTED_TILE = 5,     /* (Br, Bc) pair or dtype not built            */
+    FA_ERR_HIP = 6,                  /* the kernel launch failed                    */
+    FA_ERR_INVALID_ARG = 7           /* non-finite scale, o overlapping an input    */
+} fa_status;
+
+/* Element type codes for fa_fwd_ex. */
+enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 };
+
+/*
+ * bf16 inputs and output (q, k, v, o point to bfloat16), fp32 arithmetic
+ * inside: bf16 x bf16 products on the matrix cores with fp32 accumulation,
+ * fp32 running max/sum, probabilities rounded to bf16 (round to nearest even)
+ * only as the operand of the P V product, O rounded to bf16 once at the end.
+ * Uses the library's tuned tile shape for (d, causal).
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int N, int d, float scale, int causal,
+           const int32_t *key_len, const uint8_t *block_mask,
+           hipStream_t stream);
+
+/*
+ * fp32 inputs and output, fp32 arithmetic throughout (fp32 matrix-core
+ * products).  Same arguments and semantics as fa_fwd.
+ */
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
+               float *lse, int B, int H, int N, int d, float scale, int causal,
+               const int32_t *key_len, const uint8_t *block_mask,
+               hipStream_t stream);
+
+/*
+ * Tile-size control for the numeric-deviation study of the page "Is Flash
+ * Attention Stable?" explainer (aibr.jp, sections 3 and 4: block sizes Br and
+ * Bc varied, output compared with an FP64 golden value).  Same arguments as
+ * fa_fwd plus:
+ *   dtype : FA_DTYPE_BF16 (q/k/v/o bfloat16) or FA_DTYPE_F32 (float)
+ *   Br    : query rows per tile;  Bc : key rows per tile.
+ * Br = Bc = 0 selects the tuned default (fa_fwd / fa_fwd_f32).  bf16 builds
+ * every Br, Bc in {16, 32, 64, 128} for d = 128 and the tuned shape for
+ * d = 64; fp32 builds only its default.  Unbuilt pairs return
+ * FA_ERR_UNSUPPORTED_TILE.
+ */
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int N, int d, float scale, int causal,
+              const int32_t *key_len, const uint8_t *block_mask,
+              hipStream_t stream, int dtype, int Br, int Bc);
+
+/* Query rows (Br) and key rows (Bc) per tile that fa_fwd_ex would use for
+ * (dtype, d, Br, Bc); writes them to *br_out / *bc_out.  Returns FA_OK or
+ * FA_ERR_UNSUPPORTED_TILE / FA_ERR_UNSUPPORTED_HEAD_DIM / FA_ERR_NULL_PTR. */
+int fa_tile_shape(int dtype, int d, int Br, int Bc, int *br_out, int *bc_out);
+
+/* Static text for a status code; unknown codes give "unknown status". */
+const char *fa_status_string(int status);
+
+/* hipError_t of the most recent FA_ERR_HIP on the calling thread (0 if none). */
+int fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,165 @@
+"""Python binding of the gfx950 exact-attention forward library (libfa.so).
+
+The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
+``fa_fwd_ex``, ``fa_tile_shape``, ``fa_status_string``,
+``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
+``FaError`` on a non-zero status; every step of the attention itself runs in
+the library's HIP kernels.  ``fwd`` is a convenience wrapper that allocates
+the outputs with torch and passes torch's current stream.  There is no
+fallback: if libfa.so is missing or fails to load, every call raises.
+"""
+import ctypes
+import math
+import os
+
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_tile_shape",
+           "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
+           "DTYPE_BF16", "DTYPE_F32", "MASK_BLOCK"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+MASK_BLOCK = 128
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_INVALID_SHAPE",
+                3: "FA_ERR_UNSUPPORTED_HEAD_DIM", 4: "FA_ERR_MISALIGNED",
+                5: "FA_ERR_UNSUPPORTED_TILE", 6: "FA_ERR_HIP", 7: "FA_ERR_INVALID_ARG"}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = ""
+        if status == 6:
+            detail = f" (hipError_t {fa_last_hip_error()})"
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: "
+                         f"{fa_status_string(status)}{detail}")
+
+
+def library_path():
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python __graft_entry__.py build` "
+                           "or `python io_aware_exact_03_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    fwd_args = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp, vp, vp]
+    lib.fa_fwd.argtypes = fwd_args
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_f32.argtypes = fwd_args
+    lib.fa_fwd_f32.restype = i32
+    lib.fa_fwd_ex.argtypes = fwd_args + [i32, i32, i32]
+    lib.fa_fwd_ex.restype = i32
+    lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.fa_tile_shape.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status, where):
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+# ---------------------------------------------------------------- raw entry points
+# Pointer arguments are integers (device addresses) or None; stream is a HIP
+# stream handle as an integer (0 = default stream).
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream):
+    _check(_load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, int(bool(causal)),
+                          key_len, block_mask, stream), "fa_fwd")
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream):
+    _check(_load().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, int(bool(causal)),
+                              key_len, block_mask, stream), "fa_fwd_f32")
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream,
+              dtype, Br, Bc):
+    _check(_load().fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, int(bool(causal)),
+                             key_len, block_mask, stream, dtype, Br, Bc), "fa_fwd_ex")
+
+
+def fa_tile_shape(dtype, d, Br=0, Bc=0):
+    br, bc = ctypes.c_int(0), ctypes.c_int(0)
+    _check(_load().fa_tile_shape(dtype, d, Br, Bc, ctypes.byref(br), ctypes.byref(bc)),
+           "fa_tile_shape")
+    return br.value, bc.value
+
+
+def fa_status_string(status):
+    return _load().fa_status_string(status).decode()
+
+
+def fa_last_hip_error():
+    return int(_load().fa_last_hip_error())
+
+
+# ---------------------------------------------------------------- torch convenience
+
+
+def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, Bc=0,
+        out=None, lse=None, stream=None):
+    """Attention forward on device tensors.
+
+    q, k, v: contiguous [B, H, N, d] cuda tensors, all bfloat16 or all float32.
+    key_len: int32 cuda tensor [B] or None.  block_mask: uint8 cuda tensor with
+    ceil(N/128)^2 entries (row = query block) or None.  scale defaults to
+    1/sqrt(d).  Br/Bc = 0 selects the tuned tile.  Returns (o, lse) with o like
+    q and lse float32 [B, H, N]; `out`/`lse` may be passed preallocated, and
+    lse=False skips the logsumexp (returned as None).
+    """
+    import torch
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if q.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dtype = DTYPE_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d cuda tensor")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must share the shape [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    want_lse = lse is not False
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    kl_ptr = None
+    if key_len is not None:
+        if key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.numel() != B:
+            raise ValueError("key_len must be an int32 cuda tensor of B entries")
+        kl_ptr = key_len.data_ptr()
+    bm_ptr = None
+    if block_mask is not None:
+        nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+        if block_mask.dtype != torch.uint8 or not block_mask.is_cuda or block_mask.numel() != nb * nb:
+            raise ValueError(f"block_mask must be a uint8 cuda tensor of {nb}x{nb} entries")
+        bm_ptr = block_mask.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+              lse.data_ptr() if want_lse else None, B, H, N, d, float(scale),
+              causal, kl_ptr, bm_ptr, stream, dtype, Br, Bc)
+    return out, (lse if want_lse else None)

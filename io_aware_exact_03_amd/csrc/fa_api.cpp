@@ -1,0 +1,140 @@
+// C ABI of the attention forward library: argument validation (before any
+// HIP call), tile selection and kernel launch.  Semantics are documented in
+// include/fa.h.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool overlaps(const void *a, const void *b, uint64_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
+const fa::Instance *find(const fa::Instance *table, int d, int causal, int br, int bc) {
+    for (const fa::Instance *e = table; e->launch; ++e)
+        if (e->d == d && e->causal == causal && e->br == br && e->bc == bc) return e;
+    return nullptr;
+}
+
+// Resolves (dtype, d, Br, Bc) to the tile actually built; Br = Bc = 0 means
+// the tuned default.  Returns FA_OK or an error code.
+int resolve_tile(int dtype, int d, int br, int bc, int *br_out, int *bc_out) {
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED_TILE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (br == 0 && bc == 0) {
+        if (dtype == FA_DTYPE_BF16)
+            fa::bf16_default_tile(d, &br, &bc);
+        else
+            fa::f32_default_tile(d, &br, &bc);
+    }
+    const fa::Instance *table = dtype == FA_DTYPE_BF16 ? fa::bf16_instances() : fa::f32_instances();
+    if (!find(table, d, 0, br, bc) || !find(table, d, 1, br, bc)) return FA_ERR_UNSUPPORTED_TILE;
+    *br_out = br;
+    *bc_out = bc;
+    return FA_OK;
+}
+
+int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+            int d, float scale, int causal, const int32_t *key_len, const uint8_t *block_mask,
+            hipStream_t stream, int dtype, int br, int bc) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED_TILE;
+    // Grid size limit: B*H*ceil(N/16) workgroups at the smallest tile.
+    const uint64_t groups = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 15) / 16);
+    if (groups >= (1ull << 31)) return FA_ERR_INVALID_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return FA_ERR_MISALIGNED;
+    if ((lse && !aligned(lse, 4)) || (key_len && !aligned(key_len, 4))) return FA_ERR_MISALIGNED;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const uint64_t elem = dtype == FA_DTYPE_BF16 ? 2 : 4;
+    const uint64_t bytes = (uint64_t)B * H * N * d * elem;
+    if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
+        return FA_ERR_INVALID_ARG;
+    if (lse && overlaps(lse, o, bytes)) return FA_ERR_INVALID_ARG;
+
+    int tbr = 0, tbc = 0;
+    const int rc = resolve_tile(dtype, d, br, bc, &tbr, &tbc);
+    if (rc != FA_OK) return rc;
+    const fa::Instance *inst = find(dtype == FA_DTYPE_BF16 ? fa::bf16_instances() : fa::f32_instances(),
+                                    d, causal ? 1 : 0, tbr, tbc);
+
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.key_len = key_len;
+    a.block_mask = block_mask;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.nkb = (N + 127) / 128;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+
+    const hipError_t err = inst->launch(a, stream);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+           int d, float scale, int causal, const int32_t *key_len, const uint8_t *block_mask,
+           hipStream_t stream) {
+    return forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream,
+                   FA_DTYPE_BF16, 0, 0);
+}
+
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B, int H,
+               int N, int d, float scale, int causal, const int32_t *key_len,
+               const uint8_t *block_mask, hipStream_t stream) {
+    return forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream,
+                   FA_DTYPE_F32, 0, 0);
+}
+
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int N, int d, float scale, int causal, const int32_t *key_len,
+              const uint8_t *block_mask, hipStream_t stream, int dtype, int Br, int Bc) {
+    return forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream, dtype,
+                   Br, Bc);
+}
+
+int fa_tile_shape(int dtype, int d, int Br, int Bc, int *br_out, int *bc_out) {
+    if (!br_out || !bc_out) return FA_ERR_NULL_PTR;
+    return resolve_tile(dtype, d, Br, Bc, br_out, bc_out);
+}
+
+const char *fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL_PTR: return "null pointer argument";
+        case FA_ERR_INVALID_SHAPE: return "invalid shape (B, H, N must be >= 1 and the grid must fit)";
+        case FA_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (d must be 64 or 128)";
+        case FA_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 bytes, lse/key_len 4)";
+        case FA_ERR_UNSUPPORTED_TILE: return "unsupported dtype or tile shape";
+        case FA_ERR_HIP: return "HIP launch error (see fa_last_hip_error)";
+        case FA_ERR_INVALID_ARG: return "invalid argument (non-finite scale or overlapping output)";
+        default: return "unknown status";
+    }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

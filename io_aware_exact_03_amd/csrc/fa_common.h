@@ -1,0 +1,74 @@
+// Device helpers shared by the bf16 and fp32 forward kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+
+// Hardware base-2 exponential (v_exp_f32): exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// Reductions over the lanes that hold the same query row.  With 32x32 matrix
+// tiles a query's scores sit in lanes l and l^32; with 16x16 tiles in lanes
+// l, l^16, l^32, l^48.  v_permlane32_swap / v_permlane16_swap exchange the
+// halves without going through LDS; the two results of each swap hold the
+// value from both partner lanes, so combining them is order-independent.
+template <int MF>
+__device__ __forceinline__ float group_max(float x) {
+    if constexpr (MF == 16) {
+        auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+        x = fmaxf(u2f(r[0]), u2f(r[1]));
+    }
+    auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(r[0]), u2f(r[1]));
+}
+
+template <int MF>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (MF == 16) {
+        auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+        x = u2f(r[0]) + u2f(r[1]);
+    }
+    auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(r[0]) + u2f(r[1]);
+}
+
+// True in every lane when any lane of the wave has `pred` set.
+__device__ __forceinline__ bool wave_any(bool pred) {
+    return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+// Workgroup -> (head, query tile) order.  Workgroups are handed to the eight
+// XCDs round-robin; when the grid divides evenly, renumber so that each XCD
+// receives one contiguous run of logical tiles (whole heads where possible),
+// keeping a head's K/V re-reads inside one XCD's L2.  Causal grids visit the
+// longest query tiles of a head first.
+__device__ __forceinline__ void tile_of_block(int nqt, bool longest_first,
+                                              int *bh, int *qt) {
+    const int G = gridDim.x;
+    int id = blockIdx.x;
+    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
+    *bh = id / nqt;
+    const int r = id - *bh * nqt;
+    *qt = longest_first ? nqt - 1 - r : r;
+}
+
+}  // namespace fa

@@ -1,0 +1,43 @@
+// Internal interface between the C ABI (fa_api.cpp) and the kernel
+// translation units.  Not installed; the public interface is include/fa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a forward kernel needs, passed by value as the kernel argument.
+struct FwdArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;                 // may be null: no logsumexp written
+    const int32_t *key_len;     // may be null
+    const uint8_t *block_mask;  // may be null; ceil(N/128)^2 bytes
+    int B, H, N;
+    int nkb;                    // ceil(N/128): row length of block_mask
+    float scale_log2;           // softmax scale * log2(e), fp32
+};
+
+// Enqueues one forward pass on `stream`; returns the launch status.
+using Launcher = hipError_t (*)(const FwdArgs &, hipStream_t);
+
+// One compiled kernel instance.
+struct Instance {
+    int d;
+    int causal;
+    int br;  // query rows per workgroup tile
+    int bc;  // key rows per tile
+    Launcher launch;
+};
+
+// Tables of the instances each translation unit builds (terminated by an
+// entry with launch == nullptr), and the tuned default tile per head size.
+const Instance *bf16_instances();
+const Instance *f32_instances();
+void bf16_default_tile(int d, int *br, int *bc);
+void f32_default_tile(int d, int *br, int *bc);
+
+}  // namespace fa

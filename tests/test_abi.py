@@ -1,0 +1,95 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/fa.h declares, and rejects bad arguments with the documented
+status before any HIP call (so nothing here touches a device)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import io_aware_exact_03_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake but aligned, non-null device addresses: every call below must fail
+# validation, which happens before the library makes any HIP call.
+Q, K, V, O, LSE = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_tile_shape",
+                                           "fa_status_string", "fa_last_hip_error"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert fa.library_path().startswith(ROOT)
+
+
+def test_binding_names_match_the_abi():
+    for name in declared_functions():
+        assert callable(getattr(fa, name)), name
+
+
+def call(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, N=100, d=64, scale=0.125, causal=0,
+                key_len=None, block_mask=None, stream=None, dtype=0, Br=0, Bc=0)
+    args.update(kw)
+    lib = fa._load()
+    return lib.fa_fwd_ex(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                         args["H"], args["N"], args["d"], args["scale"], args["causal"],
+                         args["key_len"], args["block_mask"], args["stream"], args["dtype"],
+                         args["Br"], args["Bc"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(B=1 << 20, H=1 << 10, N=1 << 10), 2),
+    (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
+    (dict(q=Q + 8), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4), (dict(key_len=0x60000002), 4),
+    (dict(Br=48, Bc=64), 5), (dict(Br=128, Bc=256), 5), (dict(dtype=2), 5),
+    (dict(dtype=1, Br=16, Bc=16), 5), (dict(d=64, Br=16, Bc=16), 5),
+    (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
+    (dict(o=Q + 64), 7), (dict(lse=O + 16), 7),
+])
+def test_invalid_arguments_return_status_without_launch(kw, status):
+    assert call(**kw) == status
+    assert fa.fa_status_string(status) not in ("", "unknown status")
+
+
+def test_status_strings_cover_every_code():
+    seen = set()
+    for code in range(8):
+        s = fa.fa_status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 8
+    assert fa.fa_status_string(99) == "unknown status"
+    assert fa.fa_last_hip_error() == 0
+
+
+def test_python_wrappers_raise_with_status():
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd(Q, K, V, O, LSE, 1, 1, 16, 80, 0.1, 0, None, None, None)
+    assert e.value.status == 3
+
+
+def test_tile_table():
+    assert fa.fa_tile_shape(fa.DTYPE_BF16, 128) == (128, 64)
+    assert fa.fa_tile_shape(fa.DTYPE_BF16, 64) == (128, 64)
+    for br in (16, 32, 64, 128):
+        for bc in (16, 32, 64, 128):
+            assert fa.fa_tile_shape(fa.DTYPE_BF16, 128, br, bc) == (br, bc)
+    assert fa.fa_tile_shape(fa.DTYPE_F32, 64) == (128, 32)
+    with pytest.raises(fa.FaError):
+        fa.fa_tile_shape(fa.DTYPE_BF16, 128, 256, 64)
