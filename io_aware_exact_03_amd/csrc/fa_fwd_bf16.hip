@@ -19,23 +19,34 @@
 //   O'  = alpha*O + sum_j bf16(p_j) v_j
 // and at the end O/l, LSE = (m + log2 l) * ln 2.  l sums the fp32 p_j; the
 // bf16 rounding of p_j is used only as the operand of the P V product.
+// When no row of a wave changes its maximum, alpha is exactly 1 and the
+// rescale of O is skipped (a bit-identical no-op).
 //
-// gfx950 mapping.  One wavefront owns MF query rows (MF = 32, or 16 for the
-// small tiles of the tile-size study).  Scores are computed transposed,
-// S^T = K Q^T, on bf16 matrix-core instructions (v_mfma_f32_32x32x16_bf16 /
-// v_mfma_f32_16x16x32_bf16), so each lane holds scores of a single query
-// row: the row max and row sum are in-lane reductions plus one (or two)
-// v_permlane*_swap exchanges.  The output is accumulated transposed too,
-// O^T += V^T P^T, which takes P straight from the score registers as the B
-// operand (no LDS round trip).  Q fragments live in VGPRs for the whole
-// kernel; K tiles are stored row-major in LDS and V tiles transposed
-// (d-major) so both operands are single 16-byte LDS reads.  K/V tiles are
-// double-buffered: the global loads of tile j+1 are in flight while tile j
-// is being computed.
+// gfx950 mapping.
+//  * One wavefront owns MF query rows (MF = 32, or 16 for the small tiles of
+//    the tile-size study); a workgroup of NW waves owns BR = MF*NW rows.
+//  * Scores are computed transposed, S^T = K Q^T, on bf16 matrix-core
+//    instructions (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_16x16x32_bf16), so
+//    each lane holds scores of a single query row: row max and row sum are
+//    in-lane reductions plus v_permlane32_swap (and v_permlane16_swap).
+//  * The output is accumulated transposed too, O^T += V^T P^T, which takes P
+//    straight from the score registers as the B operand (no LDS round trip).
+//  * Q fragments live in VGPRs for the whole kernel.
+//  * K and V tiles are copied from HBM straight into LDS with
+//    global_load_lds_dwordx4 (no VGPR staging), double-buffered: the copy of
+//    tile j+1 is in flight while tile j is computed.  Both are stored
+//    row-major with an XOR swizzle of the 16-byte column slots.  K fragments
+//    are 16-byte LDS reads; V^T fragments come from ds_read_b64_tr_b16, which
+//    hands each lane one column of a 4-row block (the transpose the PV
+//    product needs).  The swizzles make both read patterns bank-conflict
+//    free.
 #include "fa_common.h"
 
 namespace fa {
 namespace {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // ----------------------------------------------------------------------------
 // Matrix-core fragment shapes.
@@ -72,134 +83,90 @@ struct Frag<16> {
     __device__ static int row(int i, int lane) { return 4 * (lane >> 4) + i; }
 };
 
-// Position of key k inside a transposed V row.  With 32x32 tiles, one PV
-// instruction consumes, in the lower half-wave, keys {0-3, 8-11} of a
-// 16-key group and in the upper half-wave keys {4-7, 12-15} (that is where
-// the score layout put them); swapping bits 2 and 3 of the key index makes
-// each half-wave's eight keys contiguous.
-template <int MF>
-__device__ __forceinline__ int vt_pos(int k) {
-    if constexpr (MF == 32)
-        return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-    else
-        return k;
-}
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-    return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xffff0000u);
-}
-
-template <int D, int BC, int MF, int NW, bool CAUSAL>
+template <int D, int BC, int MF, int NW>
 struct Cfg {
     static constexpr int NT = NW * 64;
     static constexpr int BR = MF * NW;
-    static constexpr int KSTR = D + 8;   // bf16 per K row in LDS (+16 B pad)
-    static constexpr int VSTR = BC + 8;  // bf16 per transposed V row (+16 B)
-    static constexpr int KTILE = BC * KSTR;
-    static constexpr int VTILE = D * VSTR;
-    static constexpr int NKB = BC / MF;  // score blocks per tile
-    static constexpr int ND = D / MF;    // output blocks
-    static constexpr int NQK = D / Frag<MF>::KQK;
-    static constexpr int KCH = BC * D / 8;        // 16-byte chunks of a K tile
-    static constexpr int VUN = (BC / 4) * (D / 8);  // 4-key x 8-dim V units
-    static constexpr int KPT = (KCH + NT - 1) / NT;
-    static constexpr int VPT = (VUN + NT - 1) / NT;
-    // Registers that hold one prefetched tile; beyond ~48 VGPRs the tile is
-    // loaded synchronously into a single buffer instead.
-    static constexpr bool PREFETCH = KPT * 4 + VPT * 16 <= 48;
-    static constexpr int NBUF = PREFETCH ? 2 : 1;
-    static constexpr int LDS_ELEMS = NBUF * (KTILE + VTILE);
+    static constexpr int NKB = BC / MF;            // score blocks per tile
+    static constexpr int ND = D / MF;              // output blocks
+    static constexpr int NQK = D / Frag<MF>::KQK;  // Q fragments
+    static constexpr int SLOTS = D / 8;            // 16-byte slots per row
+    static constexpr int RPL = 128 / D;            // rows per 256-byte LDS bank line
+    static constexpr int TILE = BC * D;            // bf16 per K (or V) tile
+    static constexpr int NCOPY = TILE / 512;       // 1 KiB copy instructions per tile
     static_assert(BC % MF == 0 && D % MF == 0, "tile must be a multiple of MF");
     static_assert(BC % 16 == 0 && 128 % BC == 0, "BC must divide the 128 mask block");
     static_assert(128 % BR == 0 || BR % 128 == 0, "BR and the mask block must nest");
-};
+    static_assert(TILE % 512 == 0, "tile must be a whole number of 1 KiB copies");
 
-// Per-thread staging registers of one K/V tile.
-template <class C>
-struct TileRegs {
-    u32x4_t k[C::KPT];
-    u32x4_t v[C::VPT][4];
-};
-
-// Issue the global loads of key tile `t` (rows t*BC ..) into registers.
-// Rows at or past kv_len are zero so masked keys never meet non-finite data.
-template <class C, int D, int BC>
-__device__ __forceinline__ void load_tile(TileRegs<C> &r, const __bf16 *K,
-                                          const __bf16 *V, int t, int kv_len,
-                                          int tid, int first, int count) {
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-        if (i < first || i >= first + count) continue;
-        const int c = tid + i * C::NT;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        const int key = t * BC + row;
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        if ((C::KCH % C::NT == 0 || c < C::KCH) && key < kv_len)
-            x = *reinterpret_cast<const u32x4_t *>(K + (int64_t)key * D + col8 * 8);
-        r.k[i] = x;
+    // Slot swizzle of K rows: the 16 rows read by one 16-lane group of a
+    // 16-byte read land in 16 distinct bank groups.
+    __device__ static int zk(int r) { return (r / RPL) % SLOTS; }
+    // Slot swizzle of V rows: the rows touched by one transposed read of a
+    // half-wave (4 rows x 4 slots for MF=32, 8 rows x 2 slots for MF=16)
+    // land in distinct bank groups.
+    __device__ static int zv(int r) {
+        if constexpr (MF == 32)
+            return 4 * ((r / RPL) % (D / 32));
+        else
+            return 2 * ((r / RPL) % (D / 16));
     }
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i) {
-        if (i < first || i >= first + count) continue;
-        const int u = tid + i * C::NT;
-        const int kg = u / (D / 8), col8 = u % (D / 8);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int key = t * BC + kg * 4 + rr;
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if ((C::VUN % C::NT == 0 || u < C::VUN) && key < kv_len)
-                x = *reinterpret_cast<const u32x4_t *>(V + (int64_t)key * D + col8 * 8);
-            r.v[i][rr] = x;
-        }
+};
+
+// Issue the copies of key tile rows [kbase, kbase+BC) of K and V into LDS.
+// Copy instruction q moves LDS chunks [64q, 64q+64) of the tile; chunk ci is
+// row ci/SLOTS, physical slot ci%SLOTS, which holds logical slot
+// (phys ^ swizzle(row)).  Rows past the last valid key are clamped to it:
+// those keys are masked, and the clamp keeps the data finite.
+template <class C, int D>
+__device__ __forceinline__ void copy_tile(const __bf16 *K, const __bf16 *V, __bf16 *Ks,
+                                          __bf16 *Vs, int kbase, int klast, int wave,
+                                          int lane) {
+    constexpr int ROUNDS = (C::NCOPY + C::NT / 64 - 1) / (C::NT / 64);
+#pragma unroll(ROUNDS <= 8 ? ROUNDS : 2)
+    for (int q0 = 0; q0 < C::NCOPY; q0 += C::NT / 64) {
+        const int q = q0 + wave;
+        if (C::NCOPY % (C::NT / 64) != 0 && q >= C::NCOPY) break;
+        const int ci = q * 64 + lane;
+        const int r = ci / C::SLOTS, p = ci % C::SLOTS;
+        const int64_t key = min(kbase + r, klast);
+        const __bf16 *gk = K + key * D + ((p ^ C::zk(r)) << 3);
+        const __bf16 *gv = V + key * D + ((p ^ C::zv(r)) << 3);
+        __builtin_amdgcn_global_load_lds(gk, (__attribute__((address_space(3))) void *)(Ks + q * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(gv, (__attribute__((address_space(3))) void *)(Vs + q * 512), 16, 0, 0);
     }
 }
 
-// Write staged registers into one LDS buffer: K row-major, V transposed.
-template <class C, int D, int BC, int MF>
-__device__ __forceinline__ void store_tile(const TileRegs<C> &r, __bf16 *Ks,
-                                           __bf16 *Vt, int tid, int first,
-                                           int count) {
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-        if (i < first || i >= first + count) continue;
-        const int c = tid + i * C::NT;
-        if (C::KCH % C::NT != 0 && c >= C::KCH) continue;
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        *reinterpret_cast<u32x4_t *>(Ks + row * C::KSTR + col8 * 8) = r.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i) {
-        if (i < first || i >= first + count) continue;
-        const int u = tid + i * C::NT;
-        if (C::VUN % C::NT != 0 && u >= C::VUN) continue;
-        const int kg = u / (D / 8), col8 = u % (D / 8);
-        const int pos = vt_pos<MF>(kg * 4);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // dims 2w and 2w+1 of this 8-dim chunk
-            const u32x2_t even = {pack_lo(r.v[i][0][w], r.v[i][1][w]),
-                                  pack_lo(r.v[i][2][w], r.v[i][3][w])};
-            const u32x2_t odd = {pack_hi(r.v[i][0][w], r.v[i][1][w]),
-                                 pack_hi(r.v[i][2][w], r.v[i][3][w])};
-            *reinterpret_cast<u32x2_t *>(Vt + (col8 * 8 + 2 * w) * C::VSTR + pos) = even;
-            *reinterpret_cast<u32x2_t *>(Vt + (col8 * 8 + 2 * w + 1) * C::VSTR + pos) = odd;
-        }
-    }
+__device__ __forceinline__ void wait_copies() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// V^T fragment via ds_read_b64_tr_b16: within each 16-lane group, lane i
+// points at row (i/4), columns 4*(i%4)..+3 of a 4-row x 16-column block and
+// receives column i of that block (4 consecutive rows).
+template <class C, int D>
+__device__ __forceinline__ s16x4_t read_vt(const __bf16 *Vs, int row, int col) {
+    const int off = row * D + (((col >> 3) ^ C::zv(row)) << 3) + (col & 7);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(Vs + off));
 }
 
 template <int D, int BC, int MF, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
-    using C = Cfg<D, BC, MF, NW, CAUSAL>;
+__global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf16_kernel(FwdArgs a) {
+    using C = Cfg<D, BC, MF, NW>;
     using F = Frag<MF>;
     using acc_t = typename F::acc_t;
 
-    __shared__ __attribute__((aligned(16))) __bf16 smem[C::LDS_ELEMS];
+    // Two stages of [K tile | V tile]; one array so that every LDS address
+    // of the second stage is the first stage's plus an immediate offset.
+    __shared__ __attribute__((aligned(1024))) __bf16 smem[4 * C::TILE];
+    __bf16 *const k_lds0 = smem;
+    __bf16 *const v_lds0 = smem + C::TILE;
+    __bf16 *const k_lds1 = smem + 2 * C::TILE;
+    __bf16 *const v_lds1 = smem + 3 * C::TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = a.N;
     const int nqt = (N + C::BR - 1) / C::BR;
     int bh, qt;
@@ -211,8 +178,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
     __bf16 *O = reinterpret_cast<__bf16 *>(a.o) + head;
 
-    const int q0 = qt * C::BR;      // first query row of the workgroup
-    const int wq0 = q0 + wave * MF; // first query row of this wave
+    const int q0 = qt * C::BR;       // first query row of the workgroup
+    const int wq0 = q0 + wave * MF;  // first query row of this wave
     const int qrow = wq0 + lane % MF;
 
     int kv_len = N;
@@ -220,11 +187,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     int kv_end = kv_len;
     if (CAUSAL) kv_end = min(kv_end, q0 + C::BR);
     const int ntiles = (kv_end + BC - 1) / BC;
+    const int klast = kv_len - 1;
+    // Block-sparse skipping: the mask row of this workgroup's query block is
+    // scanned 64 key blocks at a time into a wave-uniform bit mask.
     const uint8_t *mrow = a.block_mask ? a.block_mask + (int64_t)(q0 >> 7) * a.nkb : nullptr;
+    int mask_chunk = -1;
+    uint64_t mask_bits = 0;
     auto next_tile = [&](int t) {
-        if (mrow)
-            while (t < ntiles && mrow[(t * BC) >> 7] == 0) ++t;
-        return t;
+        if (!mrow || t >= ntiles) return t;
+        int blk = (t * BC) >> 7;
+        const int blk0 = blk;
+        while (blk < a.nkb) {
+            const int ch = blk >> 6;
+            if (ch != mask_chunk) {
+                const int idx = ch * 64 + lane;
+                mask_bits = __builtin_amdgcn_ballot_w64(idx < a.nkb && mrow[idx] != 0);
+                mask_chunk = ch;
+            }
+            const uint64_t rest = mask_bits >> (blk & 63);
+            if (rest) {
+                blk += __builtin_ctzll(rest);
+                break;
+            }
+            blk = (ch + 1) << 6;
+        }
+        if (blk == blk0) return t;
+        return blk >= a.nkb ? ntiles : min(ntiles, blk * (128 / BC));
     };
 
     // Q fragments (B operand of S^T = K Q^T), resident for the whole kernel.
@@ -236,8 +224,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     for (int ks = 0; ks < C::NQK; ++ks) {
         u32x4_t x = {0u, 0u, 0u, 0u};
         if (qrow < N)
-            x = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * F::KQK +
-                                                   8 * (lane / MF));
+            x = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * F::KQK + 8 * (lane / MF));
         x ^= sign;
         qf[ks] = __builtin_bit_cast(bf16x8_t, x);
     }
@@ -250,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     float m = kNegInf;  // running max of c*s for this lane's query (base 2)
     float l = 0.f;      // running sum of p over this lane's keys
 
-    auto compute = [&](int t, const __bf16 *Ks, const __bf16 *Vt) {
+    auto compute = [&](int t, const __bf16 *Ks, const __bf16 *Vs) {
         const int kbase = t * BC;
         if (wq0 >= N) return;
         if (CAUSAL && kbase > wq0 + MF - 1) return;  // whole tile above the diagonal
@@ -261,10 +248,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
             for (int i = 0; i < F::ACC; ++i) s[kb][i] = 0.f;
-            const __bf16 *kr = Ks + (kb * MF + lane % MF) * C::KSTR + 8 * (lane / MF);
+            const int r = kb * MF + lane % MF;
+            const __bf16 *kr = Ks + r * D;
+            const int z = C::zk(r);
 #pragma unroll
             for (int ks = 0; ks < C::NQK; ++ks) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(kr + ks * F::KQK);
+                const int slot = (ks * F::KQK + 8 * (lane / MF)) >> 3;
+                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(kr + ((slot ^ z) << 3));
                 s[kb] = F::qk(ka, qf[ks], s[kb]);
             }
         }
@@ -327,7 +317,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         m = m_new;
 
         // O^T += V^T P^T.
+        const int g = lane >> 4, li = lane & 15;
         if constexpr (MF == 32) {
+            // 16-key step h of block kb: the lower half-wave holds keys
+            // {0-3, 8-11}, the upper half-wave keys {4-7, 12-15} of the step
+            // (score layout); V^T takes them as two 4-row transposed reads.
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -335,10 +329,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                     bf16x8_t pf;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[kb][8 * h + j];
-                    const __bf16 *vr = Vt + (lane % 32) * C::VSTR + kb * 32 + h * 16 + 8 * (lane / 32);
+                    const int row = kb * 32 + h * 16 + 4 * (g >> 1) + (li >> 2);
+                    const int col = 16 * (g & 1) + 4 * (li & 3);
 #pragma unroll
                     for (int mb = 0; mb < C::ND; ++mb) {
-                        const bf16x8_t va = *reinterpret_cast<const bf16x8_t *>(vr + mb * 32 * C::VSTR);
+                        const s16x4_t lo = read_vt<C, D>(Vs, row, mb * 32 + col);
+                        const s16x4_t hi = read_vt<C, D>(Vs, row + 8, mb * 32 + col);
+                        const bf16x8_t va = __builtin_bit_cast(
+                            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[mb], 0, 0, 0);
                     }
                 }
@@ -348,54 +346,38 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 bf16x4_t pf;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) pf[j] = (__bf16)s[kb][j];
-                const __bf16 *vr = Vt + (lane % 16) * C::VSTR + kb * 16 + 4 * (lane / 16);
+                const int row = kb * 16 + 4 * g + (li >> 2);
+                const int col = 4 * (li & 3);
 #pragma unroll
                 for (int mb = 0; mb < C::ND; ++mb) {
-                    const bf16x4_t va = *reinterpret_cast<const bf16x4_t *>(vr + mb * 16 * C::VSTR);
+                    const s16x4_t va = read_vt<C, D>(Vs, row, mb * 16 + col);
                     o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        __builtin_bit_cast(i16x4_t, va), __builtin_bit_cast(i16x4_t, pf), o[mb], 0, 0, 0);
+                        va, __builtin_bit_cast(i16x4_t, pf), o[mb], 0, 0, 0);
                 }
             }
         }
     };
 
-    __bf16 *Ks0 = smem;
-    __bf16 *Vt0 = smem + C::KTILE;
-    TileRegs<C> regs;
+    // Double-buffered main loop, unrolled by two so each half touches fixed
+    // LDS buffers: wait for tile t, barrier (all waves are also done with the
+    // other buffer), start copying the next tile into the other buffer,
+    // compute tile t.
     int t = next_tile(0);
-    if constexpr (C::PREFETCH) {
-        __bf16 *Ks1 = smem + C::KTILE + C::VTILE;
-        __bf16 *Vt1 = Ks1 + C::KTILE;
-        if (t < ntiles) {
-            load_tile<C, D, BC>(regs, K, V, t, kv_len, tid, 0, 1 << 20);
-            store_tile<C, D, BC, MF>(regs, Ks0, Vt0, tid, 0, 1 << 20);
-        }
+    if (t < ntiles) copy_tile<C, D>(K, V, k_lds0, v_lds0, t * BC, klast, wave, lane);
+    while (t < ntiles) {
+        int tn = next_tile(t + 1);
+        wait_copies();
         __syncthreads();
-        int cur = 0;
-        while (t < ntiles) {
-            const int tn = next_tile(t + 1);
-            if (tn < ntiles) load_tile<C, D, BC>(regs, K, V, tn, kv_len, tid, 0, 1 << 20);
-            compute(t, cur ? Ks1 : Ks0, cur ? Vt1 : Vt0);
-            if (tn < ntiles) store_tile<C, D, BC, MF>(regs, cur ? Ks0 : Ks1, cur ? Vt0 : Vt1, tid, 0, 1 << 20);
-            __syncthreads();
-            cur ^= 1;
-            t = tn;
-        }
-    } else {
-        // Synchronous staging, two register batches at a time.
-        constexpr int STEP = 2;
-        constexpr int NPASS = (C::KPT > C::VPT ? C::KPT : C::VPT);
-        while (t < ntiles) {
-            __syncthreads();
-#pragma unroll
-            for (int f = 0; f < NPASS; f += STEP) {
-                load_tile<C, D, BC>(regs, K, V, t, kv_len, tid, f, STEP);
-                store_tile<C, D, BC, MF>(regs, Ks0, Vt0, tid, f, STEP);
-            }
-            __syncthreads();
-            compute(t, Ks0, Vt0);
-            t = next_tile(t + 1);
-        }
+        if (tn < ntiles) copy_tile<C, D>(K, V, k_lds1, v_lds1, tn * BC, klast, wave, lane);
+        compute(t, k_lds0, v_lds0);
+        t = tn;
+        if (t >= ntiles) break;
+        tn = next_tile(t + 1);
+        wait_copies();
+        __syncthreads();
+        if (tn < ntiles) copy_tile<C, D>(K, V, k_lds0, v_lds0, tn * BC, klast, wave, lane);
+        compute(t, k_lds1, v_lds1);
+        t = tn;
     }
 
     // Epilogue: normalise, round to bf16 once, write O and LSE.
@@ -429,7 +411,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, int BC, int MF, int NW, bool CAUSAL>
 hipError_t launch_bf16(const FwdArgs &a, hipStream_t stream) {
-    using C = Cfg<D, BC, MF, NW, CAUSAL>;
+    using C = Cfg<D, BC, MF, NW>;
     const int nqt = (a.N + C::BR - 1) / C::BR;
     const dim3 grid((unsigned)(nqt * a.B * a.H));
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, MF, NW, CAUSAL>), grid, dim3(C::NT), 0, stream, a);
