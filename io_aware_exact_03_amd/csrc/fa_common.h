@@ -51,6 +51,15 @@ __device__ __forceinline__ float group_sum(float x) {
     return u2f(r[0]) + u2f(r[1]);
 }
 
+// Multiplier c of the base-2 logits, c = |scale| * log2(e) (a negative scale
+// is folded into Q as an exact sign flip).  It is kept >= 1e-30 so that a
+// masked logit (-inf) always gives c*s - m = -inf and exp2 = 0 without a
+// select; for scale = 0 every |c*(s - max s)| stays far below half an ulp of
+// 1, so each allowed key still gets weight exactly 1.
+__device__ __forceinline__ float scale_factor(float scale_log2) {
+    return fmaxf(fabsf(scale_log2), 1e-30f);
+}
+
 // True in every lane when any lane of the wave has `pred` set.
 __device__ __forceinline__ bool wave_any(bool pred) {
     return __builtin_amdgcn_ballot_w64(pred) != 0;

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kNwF32 * 64) void fwd_f32_kernel(FwdArgs a) {
     const int ntiles = (kv_end + BC - 1) / BC;
     const uint8_t *mrow = a.block_mask ? a.block_mask + (int64_t)(q0 >> 7) * a.nkb : nullptr;
 
-    const float c = fabsf(a.scale_log2);
+    const float c = scale_factor(a.scale_log2);
     const float qsign = a.scale_log2 < 0.f ? -1.f : 1.f;
     // B operand of the 32x32x2 instruction: lane l holds Q[qrow][2*ks + l/32].
     float qf[D / 2];
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kNwF32 * 64) void fwd_f32_kernel(FwdArgs a) {
         float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float p = s[i] == kNegInf ? 0.f : fast_exp2(fmaf(s[i], c, -m_use));
+            const float p = fast_exp2(fmaf(s[i], c, -m_use));  // exp2(-inf) = 0
             s[i] = p;
             rs += p;
         }
