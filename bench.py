@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_F32_MFMA_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fa_common.h", "fa_internal.h", "fa_fwd_bf16.hip", "fa_fwd_f32.hip"]
+KERNEL_SOURCES = ["fa_common.h", "fa_internal.h", "fa_bf16_tiles.h", "fa_fwd_bf16.hip",
+                  "fa_fwd_bf16_pipe.hip", "fa_fwd_f32.hip"]
 
 
 def kernel_source_hash():
@@ -165,7 +166,8 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     scale = float(inp["scale"])
-    br, bc = fa.fa_tile_shape(0 if w.dtype == "bf16" else 1, w.d, args.br, args.bc)
+    br, bc = fa.fa_tile_shape(0 if w.dtype == "bf16" else 1, w.d, inp["block_mask"] is not None,
+                              args.br, args.bc)
 
     def step():
         fa.fwd(q, k, v, causal=w.causal, key_len=kl, block_mask=bm, scale=scale,

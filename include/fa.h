@@ -104,10 +104,11 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
  * fa_fwd plus:
  *   dtype : FA_DTYPE_BF16 (q/k/v/o bfloat16) or FA_DTYPE_F32 (float)
  *   Br    : query rows per tile;  Bc : key rows per tile.
- * Br = Bc = 0 selects the tuned default (fa_fwd / fa_fwd_f32).  bf16 builds
- * every Br, Bc in {16, 32, 64, 128} for d = 128 and the tuned shape for
- * d = 64; fp32 builds only its default.  Unbuilt pairs return
- * FA_ERR_UNSUPPORTED_TILE.
+ * Br = Bc = 0 selects the tuned default (what fa_fwd / fa_fwd_f32 use).  For
+ * bf16 every Br, Bc in {16, 32, 64, 128} is built for d = 128 (one
+ * tile-study kernel family), and the tuned shapes (Br, Bc) = (128, 64) and
+ * (256, 64) for d = 64 and 128; (256, 64) does not take a block mask.  fp32
+ * builds only its default.  Unbuilt pairs return FA_ERR_UNSUPPORTED_TILE.
  */
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N, int d, float scale, int causal,
@@ -115,9 +116,11 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               hipStream_t stream, int dtype, int Br, int Bc);
 
 /* Query rows (Br) and key rows (Bc) per tile that fa_fwd_ex would use for
- * (dtype, d, Br, Bc); writes them to *br_out / *bc_out.  Returns FA_OK or
- * FA_ERR_UNSUPPORTED_TILE / FA_ERR_UNSUPPORTED_HEAD_DIM / FA_ERR_NULL_PTR. */
-int fa_tile_shape(int dtype, int d, int Br, int Bc, int *br_out, int *bc_out);
+ * (dtype, d, block mask given or not, Br, Bc); writes them to *br_out /
+ * *bc_out.  Returns FA_OK or FA_ERR_UNSUPPORTED_TILE /
+ * FA_ERR_UNSUPPORTED_HEAD_DIM / FA_ERR_NULL_PTR. */
+int fa_tile_shape(int dtype, int d, int block_sparse, int Br, int Bc,
+                  int *br_out, int *bc_out);
 
 /* Static text for a status code; unknown codes give "unknown status". */
 const char *fa_status_string(int status);

@@ -59,7 +59,7 @@ def _load():
     lib.fa_fwd_f32.restype = i32
     lib.fa_fwd_ex.argtypes = fwd_args + [i32, i32, i32]
     lib.fa_fwd_ex.restype = i32
-    lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fa_tile_shape.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -95,10 +95,10 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, s
                              key_len, block_mask, stream, dtype, Br, Bc), "fa_fwd_ex")
 
 
-def fa_tile_shape(dtype, d, Br=0, Bc=0):
+def fa_tile_shape(dtype, d, block_sparse=False, Br=0, Bc=0):
     br, bc = ctypes.c_int(0), ctypes.c_int(0)
-    _check(_load().fa_tile_shape(dtype, d, Br, Bc, ctypes.byref(br), ctypes.byref(bc)),
-           "fa_tile_shape")
+    _check(_load().fa_tile_shape(dtype, d, int(bool(block_sparse)), Br, Bc, ctypes.byref(br),
+                                 ctypes.byref(bc)), "fa_tile_shape")
     return br.value, bc.value
 
 

@@ -14,9 +14,10 @@ thread_local int g_last_hip_error = 0;
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-bool overlaps(const void *a, const void *b, uint64_t bytes) {
+// True when the byte ranges [a, a + a_bytes) and [b, b + b_bytes) intersect.
+bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + bytes && y < x + bytes;
+    return x < y + b_bytes && y < x + a_bytes;
 }
 
 const fa::Instance *find(const fa::Instance *table, int d, int causal, int br, int bc) {
@@ -25,19 +26,28 @@ const fa::Instance *find(const fa::Instance *table, int d, int causal, int br, i
     return nullptr;
 }
 
-// Resolves (dtype, d, Br, Bc) to the tile actually built; Br = Bc = 0 means
-// the tuned default.  Returns FA_OK or an error code.
-int resolve_tile(int dtype, int d, int br, int bc, int *br_out, int *bc_out) {
+// Resolves (dtype, d, Br, Bc) to a built kernel.  Br = Bc = 0 selects the
+// tuned default for the head size (a 128-row tile when a block mask is
+// given); an explicit pair selects the tile-study kernel of that shape if
+// there is one, else a tuned kernel of that shape.  Tuned tiles taller than
+// one 128-token mask block do not take a block mask.
+int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
+                 const fa::Instance **out, int *br_out, int *bc_out) {
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED_TILE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-    if (br == 0 && bc == 0) {
-        if (dtype == FA_DTYPE_BF16)
-            fa::bf16_default_tile(d, &br, &bc);
-        else
-            fa::f32_default_tile(d, &br, &bc);
+    const fa::Instance *inst = nullptr;
+    if (dtype == FA_DTYPE_F32) {
+        if (br == 0 && bc == 0) fa::f32_default_tile(d, &br, &bc);
+        inst = find(fa::f32_instances(), d, causal, br, bc);
+    } else if (br == 0 && bc == 0) {
+        fa::bf16_default_tile(d, block_sparse, &br, &bc);
+        inst = find(fa::bf16_tuned_instances(), d, causal, br, bc);
+    } else {
+        inst = find(fa::bf16_instances(), d, causal, br, bc);
+        if (!inst && (!block_sparse || br <= 128)) inst = find(fa::bf16_tuned_instances(), d, causal, br, bc);
     }
-    const fa::Instance *table = dtype == FA_DTYPE_BF16 ? fa::bf16_instances() : fa::f32_instances();
-    if (!find(table, d, 0, br, bc) || !find(table, d, 1, br, bc)) return FA_ERR_UNSUPPORTED_TILE;
+    if (!inst) return FA_ERR_UNSUPPORTED_TILE;
+    if (out) *out = inst;
     *br_out = br;
     *bc_out = bc;
     return FA_OK;
@@ -59,15 +69,15 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
     const uint64_t elem = dtype == FA_DTYPE_BF16 ? 2 : 4;
     const uint64_t bytes = (uint64_t)B * H * N * d * elem;
-    if (overlaps(o, q, bytes) || overlaps(o, k, bytes) || overlaps(o, v, bytes))
+    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
         return FA_ERR_INVALID_ARG;
-    if (lse && overlaps(lse, o, bytes)) return FA_ERR_INVALID_ARG;
+    const uint64_t lse_bytes = (uint64_t)B * H * N * sizeof(float);
+    if (lse && overlaps(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
 
     int tbr = 0, tbc = 0;
-    const int rc = resolve_tile(dtype, d, br, bc, &tbr, &tbc);
+    const fa::Instance *inst = nullptr;
+    const int rc = resolve_tile(dtype, d, block_mask != nullptr, br, bc, causal ? 1 : 0, &inst, &tbr, &tbc);
     if (rc != FA_OK) return rc;
-    const fa::Instance *inst = find(dtype == FA_DTYPE_BF16 ? fa::bf16_instances() : fa::f32_instances(),
-                                    d, causal ? 1 : 0, tbr, tbc);
 
     fa::FwdArgs a;
     a.q = q;
@@ -116,9 +126,9 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
                    Br, Bc);
 }
 
-int fa_tile_shape(int dtype, int d, int Br, int Bc, int *br_out, int *bc_out) {
+int fa_tile_shape(int dtype, int d, int block_sparse, int Br, int Bc, int *br_out, int *bc_out) {
     if (!br_out || !bc_out) return FA_ERR_NULL_PTR;
-    return resolve_tile(dtype, d, Br, Bc, br_out, bc_out);
+    return resolve_tile(dtype, d, block_sparse ? 1 : 0, Br, Bc, 0, nullptr, br_out, bc_out);
 }
 
 const char *fa_status_string(int status) {

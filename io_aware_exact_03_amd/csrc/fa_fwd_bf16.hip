@@ -40,115 +40,10 @@
 //    hands each lane one column of a 4-row block (the transpose the PV
 //    product needs).  The swizzles make both read patterns bank-conflict
 //    free.
-#include "fa_common.h"
+#include "fa_bf16_tiles.h"
 
 namespace fa {
 namespace {
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-// ----------------------------------------------------------------------------
-// Matrix-core fragment shapes.
-
-template <int MF>
-struct Frag;
-
-// 32x32 output tile, K = 16 per instruction.  Accumulator register i of
-// lane l holds row 8*(i/4) + 4*(l/32) + i%4, column l%32.
-template <>
-struct Frag<32> {
-    using acc_t = f32x16_t;
-    static constexpr int ACC = 16;
-    static constexpr int KQK = 16;  // head-dim depth per QK instruction
-    __device__ static acc_t qk(bf16x8_t a, bf16x8_t b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static int row(int i, int lane) {
-        return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-    }
-};
-
-// 16x16 output tile, K = 32 per QK instruction and K = 16 per PV
-// instruction.  Accumulator register i of lane l holds row 4*(l/16) + i,
-// column l%16.
-template <>
-struct Frag<16> {
-    using acc_t = f32x4_t;
-    static constexpr int ACC = 4;
-    static constexpr int KQK = 32;
-    __device__ static acc_t qk(bf16x8_t a, bf16x8_t b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static int row(int i, int lane) { return 4 * (lane >> 4) + i; }
-};
-
-template <int D, int BC, int MF, int NW>
-struct Cfg {
-    static constexpr int NT = NW * 64;
-    static constexpr int BR = MF * NW;
-    static constexpr int NKB = BC / MF;            // score blocks per tile
-    static constexpr int ND = D / MF;              // output blocks
-    static constexpr int NQK = D / Frag<MF>::KQK;  // Q fragments
-    static constexpr int SLOTS = D / 8;            // 16-byte slots per row
-    static constexpr int RPL = 128 / D;            // rows per 256-byte LDS bank line
-    static constexpr int TILE = BC * D;            // bf16 per K (or V) tile
-    static constexpr int NCOPY = TILE / 512;       // 1 KiB copy instructions per tile
-    static_assert(BC % MF == 0 && D % MF == 0, "tile must be a multiple of MF");
-    static_assert(BC % 16 == 0 && 128 % BC == 0, "BC must divide the 128 mask block");
-    static_assert(128 % BR == 0 || BR % 128 == 0, "BR and the mask block must nest");
-    static_assert(TILE % 512 == 0, "tile must be a whole number of 1 KiB copies");
-
-    // Slot swizzle of K rows: the 16 rows read by one 16-lane group of a
-    // 16-byte read land in 16 distinct bank groups.
-    __device__ static int zk(int r) { return (r / RPL) % SLOTS; }
-    // Slot swizzle of V rows: the rows touched by one transposed read of a
-    // half-wave (4 rows x 4 slots for MF=32, 8 rows x 2 slots for MF=16)
-    // land in distinct bank groups.
-    __device__ static int zv(int r) {
-        if constexpr (MF == 32)
-            return 4 * ((r / RPL) % (D / 32));
-        else
-            return 2 * ((r / RPL) % (D / 16));
-    }
-};
-
-// Issue the copies of key tile rows [kbase, kbase+BC) of K and V into LDS.
-// Copy instruction q moves LDS chunks [64q, 64q+64) of the tile; chunk ci is
-// row ci/SLOTS, physical slot ci%SLOTS, which holds logical slot
-// (phys ^ swizzle(row)).  Rows past the last valid key are clamped to it:
-// those keys are masked, and the clamp keeps the data finite.
-template <class C, int D>
-__device__ __forceinline__ void copy_tile(const __bf16 *K, const __bf16 *V, __bf16 *Ks,
-                                          __bf16 *Vs, int kbase, int klast, int wave,
-                                          int lane) {
-    constexpr int ROUNDS = (C::NCOPY + C::NT / 64 - 1) / (C::NT / 64);
-#pragma unroll ROUNDS <= 8 ? ROUNDS : 2
-    for (int q0 = 0; q0 < C::NCOPY; q0 += C::NT / 64) {
-        const int q = q0 + wave;
-        if (C::NCOPY % (C::NT / 64) != 0 && q >= C::NCOPY) break;
-        const int ci = q * 64 + lane;
-        const int r = ci / C::SLOTS, p = ci % C::SLOTS;
-        const int64_t key = min(kbase + r, klast);
-        const __bf16 *gk = K + key * D + ((p ^ C::zk(r)) << 3);
-        const __bf16 *gv = V + key * D + ((p ^ C::zv(r)) << 3);
-        __builtin_amdgcn_global_load_lds(gk, (__attribute__((address_space(3))) void *)(Ks + q * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(gv, (__attribute__((address_space(3))) void *)(Vs + q * 512), 16, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void wait_copies() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// V^T fragment via ds_read_b64_tr_b16: within each 16-lane group, lane i
-// points at row (i/4), columns 4*(i%4)..+3 of a 4-row x 16-column block and
-// receives column i of that block (4 consecutive rows).
-template <class C, int D>
-__device__ __forceinline__ s16x4_t read_vt(const __bf16 *Vs, int row, int col) {
-    const int off = row * D + (((col >> 3) ^ C::zv(row)) << 3) + (col & 7);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(Vs + off));
-}
 
 template <int D, int BC, int MF, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf16_kernel(FwdArgs a) {
@@ -397,337 +292,6 @@ __global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf
     }
 }
 
-// ----------------------------------------------------------------------------
-// Tuned kernel (BR = 128, BC = 64, MF = 32): software-pipelined over key
-// tiles.  While the softmax of tile j runs on the VALU, the matrix cores
-// already compute the scores of tile j+1; while they accumulate P_j V_j the
-// VALU sums the row, packs P to bf16 and rescales O.  K is therefore staged
-// one tile ahead of V: at iteration j the LDS holds K_{j+1}, V_j and receives
-// K_{j+2}, V_{j+1}.  The interleaving is imposed with
-// __builtin_amdgcn_sched_group_barrier (groups of matrix-core, LDS-read and
-// VALU instructions), so one wave keeps both pipes busy on its own.
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x2, kSgMfma = 0x8, kSgDsRead = 0x100;
-
-template <bool B>
-struct BoolTag {
-    static constexpr bool value = B;
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_pipe(FwdArgs a) {
-    constexpr int BC = 64, MF = 32, NW = 4;
-    using C = Cfg<D, BC, MF, NW>;
-    using acc_t = f32x16_t;
-    constexpr int NQK = C::NQK, ND = C::ND;
-    constexpr int ROUNDS = C::NCOPY / NW;  // copy instructions per wave per tensor
-    static_assert(C::NCOPY % NW == 0, "copies must split evenly over the waves");
-    constexpr int QK_MFMA = 2 * NQK;       // per tile
-    constexpr int PV_MFMA = 4 * ND;        // per tile
-
-    // [K stage 0 | K stage 1 | V stage 0 | V stage 1]
-    __shared__ __attribute__((aligned(1024))) __bf16 smem[4 * C::TILE];
-    __bf16 *const K0 = smem;
-    __bf16 *const K1 = smem + C::TILE;
-    __bf16 *const V0 = smem + 2 * C::TILE;
-    __bf16 *const V1 = smem + 3 * C::TILE;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int N = a.N;
-    const int nqt = (N + C::BR - 1) / C::BR;
-    int bh, qt;
-    tile_of_block(nqt, CAUSAL, &bh, &qt);
-    const int b = bh / a.H;
-    const int64_t head = (int64_t)bh * N * D;
-    const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
-    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
-    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
-    __bf16 *O = reinterpret_cast<__bf16 *>(a.o) + head;
-
-    const int q0 = qt * C::BR;
-    const int wq0 = q0 + wave * MF;
-    const int qrow = wq0 + lane % MF;
-    int kv_len = N;
-    if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
-    int kv_end = kv_len;
-    if (CAUSAL) kv_end = min(kv_end, q0 + C::BR);
-    const int ntiles = (kv_end + BC - 1) / BC;
-    const int klast = kv_len - 1;
-    // Tiles this wave computes form a prefix of the workgroup's sequence.
-    const int wlast = wq0 >= N ? -1 : (CAUSAL ? (wq0 + MF - 1) / BC : ntiles);
-    auto active = [&](int t) { return t < ntiles && t <= wlast; };
-
-    const uint8_t *mrow = a.block_mask ? a.block_mask + (int64_t)(q0 >> 7) * a.nkb : nullptr;
-    int mask_chunk = -1;
-    uint64_t mask_bits = 0;
-    auto next_tile = [&](int t) {
-        if (!mrow || t >= ntiles) return t;
-        int blk = (t * BC) >> 7;
-        const int blk0 = blk;
-        while (blk < a.nkb) {
-            const int ch = blk >> 6;
-            if (ch != mask_chunk) {
-                const int idx = ch * 64 + lane;
-                mask_bits = __builtin_amdgcn_ballot_w64(idx < a.nkb && mrow[idx] != 0);
-                mask_chunk = ch;
-            }
-            const uint64_t rest = mask_bits >> (blk & 63);
-            if (rest) {
-                blk += __builtin_ctzll(rest);
-                break;
-            }
-            blk = (ch + 1) << 6;
-        }
-        if (blk == blk0) return t;
-        return blk >= a.nkb ? ntiles : min(ntiles, blk * (128 / BC));
-    };
-
-    // Per-lane byte offsets of this wave's copy chunks inside a tile (tile
-    // row 0 = key kbase); the tile base itself is a wave-uniform address.
-    uint32_t koff[ROUNDS], voff[ROUNDS];
-#pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) {
-        const int ci = (wave + NW * i) * 64 + lane;
-        const int r = ci / C::SLOTS, p = ci % C::SLOTS;
-        koff[i] = (uint32_t)(r * D + ((p ^ C::zk(r)) << 3)) * 2u;
-        voff[i] = (uint32_t)(r * D + ((p ^ C::zv(r)) << 3)) * 2u;
-    }
-    auto copy = [&](const __bf16 *G, __bf16 *dst, const uint32_t(&off)[ROUNDS], int t) {
-        const int kbase = t * BC;
-        const char *base = reinterpret_cast<const char *>(G + (int64_t)kbase * D);
-        if (kbase + BC <= kv_len) {
-#pragma unroll
-            for (int i = 0; i < ROUNDS; ++i)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16 *>(base + off[i]),
-                    (__attribute__((address_space(3))) void *)(dst + (wave + NW * i) * 512), 16, 0, 0);
-        } else {
-            // Last, partial tile: rows past the last valid key re-read it.
-#pragma unroll
-            for (int i = 0; i < ROUNDS; ++i) {
-                const int r = ((wave + NW * i) * 64 + lane) / C::SLOTS;
-                const int excess = max(0, kbase + r - klast);
-                __builtin_amdgcn_global_load_lds(
-                    reinterpret_cast<const __bf16 *>(base + off[i] - (uint32_t)(excess * D * 2)),
-                    (__attribute__((address_space(3))) void *)(dst + (wave + NW * i) * 512), 16, 0, 0);
-            }
-        }
-    };
-
-    // Q fragments, sign-folded so that c >= 0.
-    const float c = scale_factor(a.scale_log2);
-    const uint32_t sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-    bf16x8_t qf[NQK];
-#pragma unroll
-    for (int ks = 0; ks < NQK; ++ks) {
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        if (qrow < N)
-            x = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
-        x ^= sign;
-        qf[ks] = __builtin_bit_cast(bf16x8_t, x);
-    }
-
-    // LDS read offsets (elements): K fragment ks of a 32-key block, and the
-    // transposed V fragment of output block mb.
-    int kaddr[NQK];
-#pragma unroll
-    for (int ks = 0; ks < NQK; ++ks) {
-        const int r = lane % 32;
-        kaddr[ks] = r * D + ((((2 * ks + lane / 32)) ^ C::zk(r)) << 3);
-    }
-    const int g = lane >> 4, li = lane & 15;
-    int vaddr[ND];
-#pragma unroll
-    for (int mb = 0; mb < ND; ++mb) {
-        const int row = 4 * (g >> 1) + (li >> 2);
-        const int col = mb * 32 + 16 * (g & 1) + 4 * (li & 3);
-        vaddr[mb] = row * D + (((col >> 3) ^ C::zv(row)) << 3) + (col & 7);
-    }
-
-    acc_t o[ND];
-#pragma unroll
-    for (int mb = 0; mb < ND; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
-    float m = kNegInf, l = 0.f;
-    // Scores ping-pong between sA and sB across the two halves of the
-    // unrolled main loop (no register copies between tiles).
-    acc_t sA[2], sB[2];
-
-    auto qk_plain = [&](acc_t (&dst)[2], const __bf16 *Ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) dst[kb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < NQK; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + kb * 32 * D + kaddr[ks]);
-                dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], dst[kb], 0, 0, 0);
-            }
-    };
-
-    // One pipeline step: softmax + PV of tile t (scores in s), and the
-    // scores of the next tile (from Kn) into sn.  The QK products are issued
-    // even when this wave has no next tile (the result is then unused): a
-    // branch would split the scheduling region that interleaves the pipes.
-    auto step = [&](int t, acc_t (&s)[2], acc_t (&sn)[2], const __bf16 *Kn, const __bf16 *Vs) {
-        const int kbase = t * BC;
-        const bool edge = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
-        if (edge) {
-            // Keep this a branch: the compiler would otherwise if-convert it
-            // into per-element selects on every tile.
-            asm volatile("" ::);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kbase + kb * 32 + Frag<32>::row(i, lane);
-                    const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
-                    s[kb][i] = ok ? s[kb][i] : kNegInf;
-                }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = group_max<32>(mx);
-        const float m_tile = mx == kNegInf ? kNegInf : mx * c;
-        const float m_new = fmaxf(m, m_tile);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        const float neg_m = -m_use;
-        m = m_new;
-
-        // Phase A: QK of the next tile on the matrix cores || exponentials of
-        // this tile on the VALU (masked keys: exp2(-inf) = 0).
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sn[kb][i] = 0.f;
-        constexpr int PER = 32 / QK_MFMA;  // exponentials per QK instruction
-#pragma unroll
-        for (int ks = 0; ks < NQK; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Kn + kb * 32 * D + kaddr[ks]);
-                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sn[kb], 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < PER; ++e) {
-                    const int idx = (ks * 2 + kb) * PER + e;
-                    s[idx >> 4][idx & 15] = fast_exp2(fmaf(s[idx >> 4][idx & 15], c, neg_m));
-                }
-            }
-        // K reads run three instructions ahead of their products.
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 3, 0);
-#pragma unroll
-        for (int i = 0; i < QK_MFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            if (i + 3 < QK_MFMA) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgValu, 2 * PER, 0);
-        }
-
-        // Phase B: O^T = alpha*O^T + V^T P^T on the matrix cores || row sum,
-        // bf16 packing and the rescale on the VALU.
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bf16x8_t pf;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    pf[j] = (__bf16)s[kb][8 * h + j];
-                    rs += s[kb][8 * h + j];
-                }
-#pragma unroll
-                for (int mb = 0; mb < ND; ++mb) {
-                    if (kb == 0 && h == 0) {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
-                    }
-                    const __bf16 *vp = Vs + (kb * 32 + h * 16) * D + vaddr[mb];
-                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
-                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vp + 8 * D));
-                    const bf16x8_t va = __builtin_bit_cast(
-                        bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[mb], 0, 0, 0);
-                }
-            }
-        constexpr int VALU_B = (16 * ND + 32 + 16) / PV_MFMA + 1;
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 1);
-#pragma unroll
-        for (int i = 0; i < PV_MFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
-            if (i + 2 < PV_MFMA) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 1);
-            __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_B, 1);
-        }
-        l = fmaf(l, alpha, rs);
-    };
-
-    int t = next_tile(0);
-    int tn = next_tile(t + 1);
-    if (t < ntiles) {
-        copy(K, K0, koff, t);
-        copy(V, V0, voff, t);
-    }
-    if (tn < ntiles) copy(K, K1, koff, tn);
-    wait_copies();
-    __syncthreads();
-    if (active(t)) qk_plain(sA, K0);
-
-    // Stage parity p: K_{tn} is read from K[1-p], V_t from V[p]; K_{tnn} is
-    // copied into K[p] and V_{tn} into V[1-p].
-    while (t < ntiles) {
-        int tnn = next_tile(tn + 1);
-        wait_copies();
-        __syncthreads();
-        if (tnn < ntiles) copy(K, K0, koff, tnn);
-        if (tn < ntiles) copy(V, V1, voff, tn);
-        if (active(t)) step(t, sA, sB, K1, V0);
-        t = tn;
-        tn = tnn;
-        if (t >= ntiles) break;
-        tnn = next_tile(tn + 1);
-        wait_copies();
-        __syncthreads();
-        if (tnn < ntiles) copy(K, K1, koff, tnn);
-        if (tn < ntiles) copy(V, V0, voff, tn);
-        if (active(t)) step(t, sB, sA, K0, V1);
-        t = tn;
-        tn = tnn;
-    }
-
-    const float l_tot = group_sum<32>(l);
-    if (qrow < N) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        __bf16 *orow = O + (int64_t)qrow * D;
-#pragma unroll
-        for (int mb = 0; mb < ND; ++mb)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                bf16x4_t w;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[mb][4 * gg + j] * inv);
-                *reinterpret_cast<bf16x4_t *>(orow + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
-            }
-        if (a.lse && lane < 32)
-            a.lse[(int64_t)bh * N + qrow] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
-    }
-}
-
-template <int D, bool CAUSAL>
-hipError_t launch_pipe(const FwdArgs &a, hipStream_t stream) {
-    const int nqt = (a.N + 127) / 128;
-    hipLaunchKernelGGL((fwd_bf16_pipe<D, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(256), 0,
-                       stream, a);
-    return hipGetLastError();
-}
-
 template <int D, int BC, int MF, int NW, bool CAUSAL>
 hipError_t launch_bf16(const FwdArgs &a, hipStream_t stream) {
     using C = Cfg<D, BC, MF, NW>;
@@ -756,26 +320,15 @@ struct Pick {
 }  // namespace
 
 const Instance *bf16_instances() {
+    // Tile-size study: every (Br, Bc) in {16, 32, 64, 128}^2 for d = 128.
     static const Instance table[] = {
-        // tuned, software-pipelined shape (first match wins)
-        Instance{64, 0, 128, 64, &launch_pipe<64, false>},
-        Instance{64, 1, 128, 64, &launch_pipe<64, true>},
-        Instance{128, 0, 128, 64, &launch_pipe<128, false>},
-        Instance{128, 1, 128, 64, &launch_pipe<128, true>},
-        // tile-size study shapes
         FA_BF16_ROW(128, 16),
         FA_BF16_ROW(128, 32),
-        FA_BF16_BOTH(128, 64, 16), FA_BF16_BOTH(128, 64, 32), FA_BF16_BOTH(128, 64, 64), FA_BF16_BOTH(128, 64, 128),
-        FA_BF16_BOTH(128, 128, 16), FA_BF16_BOTH(128, 128, 32), FA_BF16_BOTH(128, 128, 128),
+        FA_BF16_ROW(128, 64),
+        FA_BF16_ROW(128, 128),
         Instance{0, 0, 0, 0, nullptr},
     };
     return table;
-}
-
-void bf16_default_tile(int d, int *br, int *bc) {
-    (void)d;
-    *br = 128;
-    *bc = 64;
 }
 
 }  // namespace fa

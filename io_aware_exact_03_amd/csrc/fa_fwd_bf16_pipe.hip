@@ -1,0 +1,450 @@
+// Tuned exact-attention forward for gfx950 (bf16 in/out, fp32 accumulation).
+//
+// Same method and running-statistics recurrence as the tile-study kernel in
+// fa_fwd_bf16.hip (tiled exact attention with an online softmax: page
+// "FlashAttention: Fast and Memory-Efficient Exact Attention with
+// IO-Awareness", ai-paper-library, Summary and Method; five-stage map of
+// "What is FlashAttention?", unite.ai), reorganised for throughput:
+//
+//  * Software pipeline over key tiles.  While the VALU exponentiates the
+//    scores of tile j, the matrix cores already compute the scores of tile
+//    j+1; while the matrix cores accumulate P_j V_j, the VALU sums the rows,
+//    packs P to bf16 and rescales O.  The interleaving is imposed with
+//    __builtin_amdgcn_sched_group_barrier, so one wave keeps both pipes busy
+//    by itself.
+//  * Each wave owns QB blocks of 32 query rows (QB = 2: 64 rows).  Every K
+//    or V fragment read from LDS then feeds QB matrix-core instructions,
+//    which halves LDS read traffic per flop, and a workgroup of 4 waves
+//    covers 128*QB query rows, which halves the HBM/L2 -> LDS traffic of the
+//    K/V stream.
+//  * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging) through an NSTAGE-deep ring: K runs one tile ahead of V (it is
+//    consumed one iteration earlier) and the copies are issued NSTAGE-1
+//    tiles ahead of use.
+//  * Scores are computed transposed (S^T = K Q^T) so each lane holds one
+//    query row: the row max is an in-lane v_max3 chain plus one
+//    v_permlane32_swap; O^T += V^T P^T takes P straight from registers.
+#include "fa_bf16_tiles.h"
+
+namespace fa {
+namespace {
+
+template <int D, int QB, int BC, int NSTAGE, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf16_pipe(FwdArgs a) {
+    constexpr int QW = 32 * QB, BR = QW * NW, NKB = BC / 32;
+    using C = Cfg<D, BC, 32, NW>;
+    using acc_t = f32x16_t;
+    constexpr int NQK = C::NQK, ND = C::ND;
+    constexpr int ROUNDS = C::NCOPY / NW;  // copy instructions per wave per tensor
+    static_assert(C::NCOPY % NW == 0, "copies must split evenly over the waves");
+    constexpr int P = NSTAGE - 1;          // copies run P tiles ahead
+    static_assert(P >= 1 && P <= 3, "2..4 stages");
+    constexpr int QK_MFMA = NKB * NQK * QB;     // per tile
+    constexpr int PV_MFMA = NKB * 2 * ND * QB;  // per tile
+
+    // One LDS array per K stage and per V stage.
+    __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 k_lds2[NSTAGE > 2 ? C::TILE : 1];
+    __shared__ __attribute__((aligned(1024))) __bf16 k_lds3[NSTAGE > 3 ? C::TILE : 1];
+    __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 v_lds2[NSTAGE > 2 ? C::TILE : 1];
+    __shared__ __attribute__((aligned(1024))) __bf16 v_lds3[NSTAGE > 3 ? C::TILE : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = a.N;
+    const int nqt = (N + BR - 1) / BR;
+    int bh, qt;
+    tile_of_block(nqt, CAUSAL, &bh, &qt);
+    const int b = bh / a.H;
+    const int64_t head = (int64_t)bh * N * D;
+    const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
+    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
+    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
+    __bf16 *O = reinterpret_cast<__bf16 *>(a.o) + head;
+
+    const int q0 = qt * BR;
+    const int wq0 = q0 + wave * QW;
+    int kv_len = N;
+    if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
+    int kv_end = kv_len;
+    if (CAUSAL) kv_end = min(kv_end, q0 + BR);
+    const int ntiles = (kv_end + BC - 1) / BC;
+    const int klast = kv_len - 1;
+    // Tiles this wave computes form a prefix of the workgroup's sequence.
+    const int wlast = wq0 >= N ? -1 : (CAUSAL ? (wq0 + QW - 1) / BC : ntiles);
+    auto active = [&](int t) { return t < ntiles && t <= wlast; };
+
+    // Block-sparse skipping (only launched with BR = 128, where the
+    // workgroup's rows are one query block): the mask row is scanned 64 key
+    // blocks at a time into a wave-uniform bit mask.
+    const uint8_t *mrow = a.block_mask ? a.block_mask + (int64_t)(q0 >> 7) * a.nkb : nullptr;
+    int mask_chunk = -1;
+    uint64_t mask_bits = 0;
+    auto next_tile = [&](int t) {
+        if (!mrow || t >= ntiles) return t;
+        int blk = (t * BC) >> 7;
+        const int blk0 = blk;
+        while (blk < a.nkb) {
+            const int ch = blk >> 6;
+            if (ch != mask_chunk) {
+                const int idx = ch * 64 + lane;
+                mask_bits = __builtin_amdgcn_ballot_w64(idx < a.nkb && mrow[idx] != 0);
+                mask_chunk = ch;
+            }
+            const uint64_t rest = mask_bits >> (blk & 63);
+            if (rest) {
+                blk += __builtin_ctzll(rest);
+                break;
+            }
+            blk = (ch + 1) << 6;
+        }
+        if (blk == blk0) return t;
+        return blk >= a.nkb ? ntiles : min(ntiles, blk * (128 / BC));
+    };
+
+    // Per-lane byte offsets of this wave's copy chunks inside a tile; the
+    // tile base is a wave-uniform address.
+    uint32_t koff[ROUNDS], voff[ROUNDS];
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+        const int ci = (wave + NW * i) * 64 + lane;
+        const int r = ci / C::SLOTS, p = ci % C::SLOTS;
+        koff[i] = (uint32_t)(r * D + ((p ^ C::zk(r)) << 3)) * 2u;
+        voff[i] = (uint32_t)(r * D + ((p ^ C::zv(r)) << 3)) * 2u;
+    }
+    auto copy = [&](const __bf16 *G, __bf16 *dst, const uint32_t(&off)[ROUNDS], int t) {
+        const int kbase = t * BC;
+        const char *base = reinterpret_cast<const char *>(G + (int64_t)kbase * D);
+        if (kbase + BC <= kv_len) {
+#pragma unroll
+            for (int i = 0; i < ROUNDS; ++i) lds_copy16(base, off[i], dst + (wave + NW * i) * 512);
+        } else {
+            // Last, partial tile: rows past the last valid key re-read it.
+#pragma unroll
+            for (int i = 0; i < ROUNDS; ++i) {
+                const int r = ((wave + NW * i) * 64 + lane) / C::SLOTS;
+                const int excess = max(0, kbase + r - klast);
+                lds_copy16(base, off[i] - (uint32_t)(excess * D * 2), dst + (wave + NW * i) * 512);
+            }
+        }
+    };
+    auto kstage = [&](int s) { return s == 0 ? k_lds0 : s == 1 ? k_lds1 : s == 2 ? k_lds2 : k_lds3; };
+    auto vstage = [&](int s) { return s == 0 ? v_lds0 : s == 1 ? v_lds1 : s == 2 ? v_lds2 : v_lds3; };
+
+    // Q fragments (B operand of S^T = K Q^T), sign-folded so that c >= 0.
+    const float c = scale_factor(a.scale_log2);
+    const uint32_t sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+    bf16x8_t qf[QB][NQK];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = wq0 + 32 * qb + lane % 32;
+#pragma unroll
+        for (int ks = 0; ks < NQK; ++ks) {
+            u32x4_t x = {0u, 0u, 0u, 0u};
+            if (qrow < N)
+                x = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
+            x ^= sign;
+            qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+
+    // LDS read offsets (elements): K fragment ks of a 32-key block, and the
+    // transposed V fragment of output block mb (two 4-row reads, 8 rows apart).
+    // K: row r starts at a multiple of 2*D bytes and the swizzled slot
+    // (2ks + lane/32) ^ zk(r) fits in the low bits, so the element offset is
+    // kbase0 ^ (16*ks): one base register instead of NQK.
+    const int kbase0 = (lane % 32) * D + (((lane / 32) ^ C::zk(lane % 32)) << 3);
+    const int g = lane >> 4, li = lane & 15;
+    int vaddr[ND];
+#pragma unroll
+    for (int mb = 0; mb < ND; ++mb) {
+        const int row = 4 * (g >> 1) + (li >> 2);
+        const int col = mb * 32 + 16 * (g & 1) + 4 * (li & 3);
+        vaddr[mb] = row * D + (((col >> 3) ^ C::zv(row)) << 3) + (col & 7);
+    }
+
+    acc_t o[QB][ND];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[qb][mb][i] = 0.f;
+    float m[QB], l[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = kNegInf;
+        l[qb] = 0.f;
+    }
+    // Scores ping-pong between sA and sB across consecutive iterations.
+    acc_t sA[QB][NKB], sB[QB][NKB];
+
+    auto qk_plain = [&](acc_t (&dst)[QB][NKB], const __bf16 *Ks) {
+        auto kaddr = [&](int ks) { return kbase0 ^ (ks << 4); };
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dst[qb][kb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NQK; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + kb * 32 * D + kaddr(ks));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    dst[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], dst[qb][kb], 0, 0, 0);
+            }
+    };
+
+    // One pipeline step: softmax + PV of tile t (scores in s), and the
+    // scores of the next tile (from Kn) into sn.  The QK products are issued
+    // even when this wave has no next tile (the result is then unused): a
+    // branch would split the scheduling region that interleaves the pipes.
+    auto step = [&](int t, acc_t (&s)[QB][NKB], acc_t (&sn)[QB][NKB], const __bf16 *Kn,
+                    const __bf16 *Vs) {
+        const int kbase = t * BC;
+        const bool edge = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
+        if (edge) {
+            // Keep this a branch: the compiler would otherwise if-convert it
+            // into per-element selects on every tile.
+            asm volatile("" ::);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int qrow = wq0 + 32 * qb + lane % 32;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kbase + kb * 32 + Frag<32>::row(i, lane);
+                        const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
+                        s[qb][kb][i] = ok ? s[qb][kb][i] : kNegInf;
+                    }
+            }
+        }
+        float alpha[QB], neg_m[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+            mx = group_max<32>(mx);
+            const float m_tile = mx == kNegInf ? kNegInf : mx * c;
+            const float m_new = fmaxf(m[qb], m_tile);
+            const float m_use = m_new == kNegInf ? 0.f : m_new;
+            alpha[qb] = fast_exp2(m[qb] - m_use);
+            neg_m[qb] = -m_use;
+            m[qb] = m_new;
+        }
+
+        // The K read offsets are rederived from kbase0 in every step (one XOR
+        // each) rather than kept live as NQK loop-invariant registers; the
+        // empty asm stops the compiler from hoisting them out of the loop.
+        int kb0 = kbase0;
+        asm volatile("" : "+v"(kb0));
+        auto kaddr = [&](int ks) { return kb0 ^ (ks << 4); };
+
+        // Phase A: QK of the next tile on the matrix cores || exponentials of
+        // this tile on the VALU (masked keys: exp2(-inf) = 0).
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sn[qb][kb][i] = 0.f;
+        constexpr int PER = 16 * NKB * QB / QK_MFMA;  // exponentials per QK instruction
+        int e_next = 0;
+#pragma unroll
+        for (int ks = 0; ks < NQK; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Kn + kb * 32 * D + kaddr(ks));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    sn[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], sn[qb][kb], 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < PER; ++e, ++e_next) {
+                        const int eq = e_next / (16 * NKB), ek = (e_next / 16) % NKB, ei = e_next & 15;
+                        s[eq][ek][ei] = fast_exp2(fmaf(s[eq][ek][ei], c, neg_m[eq]));
+                    }
+                }
+            }
+        // K reads run ahead of their products.
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+#pragma unroll
+        for (int i = 0; i < QK_MFMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            if (i % QB == 0 && i / QB + 2 < NKB * NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgValu, 2 * PER, 0);
+        }
+
+        // Phase B: O^T = alpha*O^T + V^T P^T on the matrix cores || row sum,
+        // bf16 packing and the rescale on the VALU.
+        float rs[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8_t pf[QB];
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        pf[qb][j] = (__bf16)s[qb][kb][8 * h + j];
+                        rs[qb] += s[qb][kb][8 * h + j];
+                    }
+#pragma unroll
+                for (int mb = 0; mb < ND; ++mb) {
+                    const __bf16 *vp = Vs + (kb * 32 + h * 16) * D + vaddr[mb];
+                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
+                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vp + 8 * D));
+                    const bf16x8_t va = __builtin_bit_cast(
+                        bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        if (kb == 0 && h == 0) {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) o[qb][mb][i] *= alpha[qb];
+                        }
+                        o[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb], o[qb][mb], 0, 0, 0);
+                    }
+                }
+            }
+        constexpr int VALU_B = (16 * ND + 24 * NKB) * QB / PV_MFMA + 1;
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 1);
+#pragma unroll
+        for (int i = 0; i < PV_MFMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
+            if (i % QB == 0 && i / QB + 2 < 2 * NKB * ND) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_B, 1);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l[qb] = fmaf(l[qb], alpha[qb], rs[qb]);
+    };
+
+    // ---- pipeline ---------------------------------------------------------
+    // Tile sequence T[0], T[1], ... (active tiles of the workgroup); tq[j]
+    // holds T[i+j] for j = 0..P at iteration i.  Iteration i computes the
+    // softmax/PV of T[i] (scores already in registers) and the scores of
+    // T[i+1]; it needs K(T[i+1]) in K stage (i+1)%NSTAGE and V(T[i]) in V
+    // stage i%NSTAGE, and it starts the copies of K(T[i+1+P]) into K stage
+    // i%NSTAGE and of V(T[i+P]) into V stage (i-1)%NSTAGE, both freed by the
+    // previous iteration.
+    int tq[P + 1];
+    tq[0] = next_tile(0);
+#pragma unroll
+    for (int j = 1; j <= P; ++j) tq[j] = next_tile(tq[j - 1] + 1);
+#pragma unroll
+    for (int j = 0; j <= P; ++j)
+        if (tq[j] < ntiles) copy(K, kstage(j), koff, tq[j]);
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (tq[j] < ntiles) copy(V, vstage(j), voff, tq[j]);
+    wait_copies();
+    __syncthreads();
+    if (active(tq[0])) qk_plain(sA, kstage(0));
+
+    auto iteration = [&](auto stage_tag, acc_t (&s)[QB][NKB], acc_t (&sn)[QB][NKB]) {
+        constexpr int u = decltype(stage_tag)::value;  // i % NSTAGE
+        const int t_new = next_tile(tq[P] + 1);         // T[i+P+1]
+        // Copies younger than those of K(T[i+1]) and V(T[i]) were issued in
+        // the last P-1 iterations; they may stay in flight when complete.
+        if (P > 1 && tq[P] < ntiles)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * ROUNDS * (P - 1)) : "memory");
+        else
+            wait_copies();
+        stage_barrier();
+        if (t_new < ntiles) copy(K, kstage(u), koff, t_new);
+        if (tq[P] < ntiles) copy(V, vstage((u + NSTAGE - 1) % NSTAGE), voff, tq[P]);
+        if (active(tq[0])) step(tq[0], s, sn, kstage((u + 1) % NSTAGE), vstage(u));
+#pragma unroll
+        for (int j = 0; j < P; ++j) tq[j] = tq[j + 1];
+        tq[P] = t_new;
+    };
+
+    while (true) {
+        if (tq[0] >= ntiles) break;
+        iteration(IntTag<0>{}, sA, sB);
+        if (tq[0] >= ntiles) break;
+        iteration(IntTag<1 % NSTAGE>{}, sB, sA);
+        if constexpr (NSTAGE % 2 == 1 || NSTAGE == 4) {
+            // Unrolled to a multiple of both NSTAGE and 2 (score ping-pong).
+            if (tq[0] >= ntiles) break;
+            iteration(IntTag<2 % NSTAGE>{}, sA, sB);
+            if (tq[0] >= ntiles) break;
+            iteration(IntTag<3 % NSTAGE>{}, sB, sA);
+            if constexpr (NSTAGE == 3) {
+                if (tq[0] >= ntiles) break;
+                iteration(IntTag<4 % NSTAGE>{}, sA, sB);
+                if (tq[0] >= ntiles) break;
+                iteration(IntTag<5 % NSTAGE>{}, sB, sA);
+            }
+        }
+    }
+
+    // Epilogue: normalise, round to bf16 once, write O and LSE.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = wq0 + 32 * qb + lane % 32;
+        const float l_tot = group_sum<32>(l[qb]);
+        if (qrow < N) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            __bf16 *orow = O + (int64_t)qrow * D;
+#pragma unroll
+            for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    bf16x4_t w;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[qb][mb][4 * gg + j] * inv);
+                    *reinterpret_cast<bf16x4_t *>(orow + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
+                }
+            if (a.lse && lane < 32)
+                a.lse[(int64_t)bh * N + qrow] = l_tot > 0.f ? (m[qb] + fast_log2(l_tot)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+template <int D, int QB, int BC, int NSTAGE, int NW, bool CAUSAL>
+hipError_t launch_pipe(const FwdArgs &a, hipStream_t stream) {
+    constexpr int BR = 32 * QB * NW;
+    const int nqt = (a.N + BR - 1) / BR;
+    hipLaunchKernelGGL((fwd_bf16_pipe<D, QB, BC, NSTAGE, NW, CAUSAL>),
+                       dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+#define FA_PIPE(D, QB, BC, NS, NW) \
+    Instance{D, 0, 32 * QB * NW, BC, &launch_pipe<D, QB, BC, NS, NW, false>}, \
+    Instance{D, 1, 32 * QB * NW, BC, &launch_pipe<D, QB, BC, NS, NW, true>}
+
+}  // namespace
+
+const Instance *bf16_tuned_instances() {
+    static const Instance table[] = {
+        FA_PIPE(64, 1, 64, 2, 4),
+        FA_PIPE(64, 1, 64, 2, 8),
+        FA_PIPE(128, 1, 64, 2, 4),
+        FA_PIPE(128, 1, 64, 2, 8),
+        Instance{0, 0, 0, 0, nullptr},
+    };
+    return table;
+}
+
+void bf16_default_tile(int d, int block_sparse, int *br, int *bc) {
+    (void)d;
+    (void)block_sparse;
+    *br = 128;
+    *bc = 64;
+}
+
+}  // namespace fa

@@ -34,10 +34,13 @@ struct Instance {
 };
 
 // Tables of the instances each translation unit builds (terminated by an
-// entry with launch == nullptr), and the tuned default tile per head size.
+// entry with launch == nullptr): the tuned bf16 kernels, the bf16
+// tile-size-study kernels and the fp32 kernels; and the default tile per head
+// size.  Tuned bf16 tiles with Br > 128 do not take a block mask.
+const Instance *bf16_tuned_instances();
 const Instance *bf16_instances();
 const Instance *f32_instances();
-void bf16_default_tile(int d, int *br, int *bc);
+void bf16_default_tile(int d, int block_sparse, int *br, int *bc);
 void f32_default_tile(int d, int *br, int *bc);
 
 }  // namespace fa

@@ -59,8 +59,9 @@ def call(**kw):
     (dict(q=Q + 8), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4), (dict(key_len=0x60000002), 4),
     (dict(Br=48, Bc=64), 5), (dict(Br=128, Bc=256), 5), (dict(dtype=2), 5),
     (dict(dtype=1, Br=16, Bc=16), 5), (dict(d=64, Br=16, Bc=16), 5),
+    (dict(Br=256, Bc=64, block_mask=0x70000000), 5),
     (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
-    (dict(o=Q + 64), 7), (dict(lse=O + 16), 7),
+    (dict(o=Q + 64), 7), (dict(lse=O + 16), 7), (dict(lse=O - 2 * 3 * 100 * 4 + 4), 7),
 ])
 def test_invalid_arguments_return_status_without_launch(kw, status):
     assert call(**kw) == status
@@ -85,11 +86,21 @@ def test_python_wrappers_raise_with_status():
 
 
 def test_tile_table():
-    assert fa.fa_tile_shape(fa.DTYPE_BF16, 128) == (128, 64)
-    assert fa.fa_tile_shape(fa.DTYPE_BF16, 64) == (128, 64)
+    for d in (64, 128):
+        br, bc = fa.fa_tile_shape(fa.DTYPE_BF16, d)
+        assert br in (128, 256) and bc in (32, 64)
+        # the default is itself a built, explicitly selectable tile
+        assert fa.fa_tile_shape(fa.DTYPE_BF16, d, False, br, bc) == (br, bc)
+        # a block mask needs a tile no taller than one 128-token mask block
+        br, bc = fa.fa_tile_shape(fa.DTYPE_BF16, d, block_sparse=True)
+        assert br <= 128
     for br in (16, 32, 64, 128):
         for bc in (16, 32, 64, 128):
-            assert fa.fa_tile_shape(fa.DTYPE_BF16, 128, br, bc) == (br, bc)
+            assert fa.fa_tile_shape(fa.DTYPE_BF16, 128, False, br, bc) == (br, bc)
+    assert fa.fa_tile_shape(fa.DTYPE_BF16, 64, False, 128, 64) == (128, 64)
+    assert fa.fa_tile_shape(fa.DTYPE_BF16, 128, False, 256, 64) == (256, 64)
     assert fa.fa_tile_shape(fa.DTYPE_F32, 64) == (128, 32)
     with pytest.raises(fa.FaError):
-        fa.fa_tile_shape(fa.DTYPE_BF16, 128, 256, 64)
+        fa.fa_tile_shape(fa.DTYPE_BF16, 128, True, 256, 64)
+    with pytest.raises(fa.FaError):
+        fa.fa_tile_shape(fa.DTYPE_BF16, 64, False, 16, 16)

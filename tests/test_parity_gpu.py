@@ -268,6 +268,19 @@ def test_nonstandard_scales(scale):
     check(o, lse, *ref(inp, scale=scale), TOL_F32, f"f32 scale={scale}")
 
 
+def test_adjacent_output_buffers():
+    """LSE placed directly before O in one allocation is a valid layout."""
+    inp = custom(2, 3, 100, 64, seed=30)
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    n_lse = 2 * 3 * 100
+    raw = torch.empty(n_lse * 4 + q.numel() * 2, dtype=torch.uint8, device="cuda")
+    lse = raw[: n_lse * 4].view(torch.float32).view(2, 3, 100)
+    out = raw[n_lse * 4:].view(torch.bfloat16).view(q.shape)
+    fa.fwd(q, k, v, out=out, lse=lse)
+    torch.cuda.synchronize()
+    check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16, "adjacent")
+
+
 def test_no_lse_requested():
     inp = custom(1, 1, 100, 64, seed=29)
     q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
