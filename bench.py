@@ -140,11 +140,26 @@ def main():
     ap.add_argument("--bc", type=int, default=0, help="key rows per tile (0 = tuned)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (3 times), the known-size "
+                         "reference that scales the FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = 512 << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the attention path shards over heads with no communication, see DESIGN.md",
+              "the attention path shards over (batch, head) pairs with no communication",
               file=sys.stderr)
         sys.exit(2)
 

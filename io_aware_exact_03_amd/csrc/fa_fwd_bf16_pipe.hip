@@ -12,11 +12,11 @@
 //    packs P to bf16 and rescales O.  The interleaving is imposed with
 //    __builtin_amdgcn_sched_group_barrier, so one wave keeps both pipes busy
 //    by itself.
-//  * Each wave owns QB blocks of 32 query rows (QB = 2: 64 rows).  Every K
-//    or V fragment read from LDS then feeds QB matrix-core instructions,
-//    which halves LDS read traffic per flop, and a workgroup of 4 waves
-//    covers 128*QB query rows, which halves the HBM/L2 -> LDS traffic of the
-//    K/V stream.
+//  * Each wave owns QB blocks of 32 query rows; every K or V fragment read
+//    from LDS feeds QB matrix-core instructions.  The built instances use
+//    QB = 1: with QB = 2 the doubled accumulator set no longer fits beside
+//    the score tiles without accumulator/VGPR shuffling, which cost more
+//    than the halved LDS traffic saved.
 //  * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging) through an NSTAGE-deep ring: K runs one tile ahead of V (it is
 //    consumed one iteration earlier) and the copies are issued NSTAGE-1

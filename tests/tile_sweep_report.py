@@ -1,0 +1,85 @@
+"""Tile-size deviation study on the causal 16K-token workload's prefix slice.
+
+Block sizes Br (query rows per tile) and Bc (key rows per tile) are varied
+and each output is compared with the FP64 golden value, as in the
+micro-benchmark of the page "Is Flash Attention Stable?" (aibr.jp, sections 3
+and 4, where deviation falls as tiles grow because fewer rescalings happen).
+The slice is B=1, H=4, N=2048, d=128, causal, inputs 0.5*N(0,1) from the
+16K workload's generator: under the causal mask it is exactly rows 0..2047 of
+heads 0..3 of the full problem.
+
+For every (Br, Bc) it prints max|dO|, mean|dO|, max|dLSE| against the oracle
+and the kernel time per launch (HIP events on the launch stream).  The trend
+is reported, not asserted; the per-point bar (max|dO| <= 2e-2) is asserted by
+the GPU parity tests.
+
+    python tests/tile_sweep_report.py [--json PATH]
+"""
+import argparse
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import io_aware_exact_03_amd as fa  # noqa: E402
+import oracle  # noqa: E402
+from workloads import WORKLOADS, make_inputs  # noqa: E402
+
+PAIRS = [(br, bc) for br in (16, 32, 64, 128) for bc in (16, 32, 64, 128)] + [(256, 64), (0, 0)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--json", default=None)
+    ap.add_argument("--reps", type=int, default=20)
+    args = ap.parse_args()
+    w = WORKLOADS["long_causal"]
+    inp = make_inputs(w, N=2048, H=4)
+    scale = float(np.float32(inp["scale"]))
+    o_ref, lse_ref = oracle.attention_f64(inp["q"], inp["k"], inp["v"], scale, True, None, None, 128)
+    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    pairs = 4 * 2048 * 2049 // 2
+    rows = []
+    for br, bc in PAIRS:
+        def call():
+            fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, out=out, lse=lse)
+        call()
+        torch.cuda.synchronize()
+        o = out.double().cpu().numpy()
+        l = lse.double().cpu().numpy()
+        d_o = np.abs(o - o_ref)
+        d_l = np.abs(l - lse_ref)
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            call()
+        e0.record(s)
+        for _ in range(args.reps):
+            call()
+        e1.record(s)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.reps
+        tb, tc = fa.fa_tile_shape(0, 128, False, br, bc)
+        rows.append(dict(Br=tb, Bc=tc, default=(br, bc) == (0, 0), max_dO=float(d_o.max()),
+                         mean_dO=float(d_o.mean()), max_dLSE=float(d_l.max()), us=us,
+                         tflops=4 * 128 * pairs / (us * 1e-6) / 1e12))
+    print("| Br | Bc | max abs dO | mean abs dO | max abs dLSE | us/launch | TFLOP/s |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        tag = " (default)" if r["default"] else ""
+        print(f"| {r['Br']}{tag} | {r['Bc']} | {r['max_dO']:.3e} | {r['mean_dO']:.3e} | "
+              f"{r['max_dLSE']:.3e} | {r['us']:.1f} | {r['tflops']:.1f} |", flush=True)
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()
