@@ -3,6 +3,8 @@
 // transposed V read.  Internal header.
 #pragma once
 
+#include <utility>
+
 #include "fa_common.h"
 
 namespace fa {
@@ -146,14 +148,23 @@ __device__ __forceinline__ s16x4_t read_vt(const __bf16 *Vs, int row, int col) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(Vs + off));
 }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x2, kSgMfma = 0x8, kSgDsRead = 0x100;
-
 // Compile-time integer carried through a generic lambda argument.
 template <int V>
 struct IntTag {
     static constexpr int value = V;
 };
+
+// f(IntTag<0>{}), f(IntTag<1>{}), ..., f(IntTag<N-1>{}): a loop whose index
+// is a constant expression in the body (guaranteed unrolling, `if constexpr`
+// on the index).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(IntTag<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace
 }  // namespace fa

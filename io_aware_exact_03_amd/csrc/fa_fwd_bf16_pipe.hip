@@ -8,15 +8,14 @@
 //
 //  * Software pipeline over key tiles.  While the VALU exponentiates the
 //    scores of tile j, the matrix cores already compute the scores of tile
-//    j+1; while the matrix cores accumulate P_j V_j, the VALU sums the rows,
-//    packs P to bf16 and rescales O.  The interleaving is imposed with
-//    __builtin_amdgcn_sched_group_barrier, so one wave keeps both pipes busy
-//    by itself.
-//  * Each wave owns QB blocks of 32 query rows; every K or V fragment read
-//    from LDS feeds QB matrix-core instructions.  The built instances use
-//    QB = 1: with QB = 2 the doubled accumulator set no longer fits beside
-//    the score tiles without accumulator/VGPR shuffling, which cost more
-//    than the halved LDS traffic saved.
+//    j+1; while the matrix cores accumulate P_j V_j, the VALU packs P to
+//    bf16 and sums the rows.  Each step is a fixed sequence of matrix-core
+//    slots with the VALU work spread over them (see `step`), so one wave
+//    keeps both pipes busy by itself.
+//  * O is rescaled only when some row of the wave raised its running
+//    maximum; otherwise the rescale factor is exactly 1 and the multiply is
+//    skipped (a bit-identical no-op).
+//  * Each wave owns 32 query rows; a workgroup of NW waves owns 32*NW.
 //  * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging) through an NSTAGE-deep ring: K runs one tile ahead of V (it is
 //    consumed one iteration earlier) and the copies are issued NSTAGE-1
@@ -29,9 +28,66 @@
 namespace fa {
 namespace {
 
-template <int D, int QB, int BC, int NSTAGE, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf16_pipe(FwdArgs a) {
-    constexpr int QW = 32 * QB, BR = QW * NW, NKB = BC / 32;
+// VALU work of one tile for one wave, cut into chunks in dependency order:
+// per 8-score fragment f (NF of them) a partial row max; the cross-lane max
+// and rescale factor; per fragment two halves of exponentials and one bf16
+// packing; per fragment a partial row sum.  Each chunk is assigned to the
+// matrix-core slot where its estimated start falls when the total VALU time
+// (fp32 op ~4 cycles, exponential ~8 cycles per wave) is spread evenly over
+// the step's NS slots.
+// Empty asm statements that make a value "used" where they stand: the
+// compiler may not sink its computation below them (past the rescale branch
+// of a step, say), which keeps the VALU work in the slot it was assigned to.
+template <class T>
+__device__ __forceinline__ void pin(T &x) {
+    asm volatile("" : "+v"(x));
+}
+__device__ __forceinline__ void pin4(float &a, float &b, float &c, float &d) {
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// Slot at which the V fragments of PV product pv are read (LB slots ahead;
+// the first ones during the QK phase).
+__host__ __device__ constexpr int vread_slot_of(int pv, int na, int lb) { return na + pv - lb; }
+
+constexpr int kChunkMax = 0, kChunkRed = 1, kChunkExp = 2, kChunkCvt = 3, kChunkSum = 4;
+
+template <int NF>
+struct ChunkPlan {
+    static constexpr int NCH = 5 * NF + 1;
+    __host__ __device__ static constexpr int kind(int k) {
+        return k < NF ? kChunkMax
+             : k == NF ? kChunkRed
+             : k < 4 * NF + 1 ? ((k - NF - 1) % 3 == 2 ? kChunkCvt : kChunkExp)
+             : kChunkSum;
+    }
+    __host__ __device__ static constexpr int frag(int k) {
+        return k < NF ? k : k == NF ? 0 : k < 4 * NF + 1 ? (k - NF - 1) / 3 : k - 4 * NF - 1;
+    }
+    __host__ __device__ static constexpr int half(int k) { return (k - NF - 1) % 3; }
+    __host__ __device__ static constexpr int cost(int k) {
+        return kind(k) == kChunkMax ? 16 : kind(k) == kChunkRed ? 48 : kind(k) == kChunkExp ? 48
+             : kind(k) == kChunkCvt ? 16 : 32;
+    }
+    __host__ __device__ static constexpr int start(int k) {
+        int c = 0;
+        for (int i = 0; i < k; ++i) c += cost(i);
+        return c;
+    }
+    __host__ __device__ static constexpr int slot(int k, int ns) { return start(k) * ns / start(NCH); }
+    // Slot of the packing of fragment f.
+    __host__ __device__ static constexpr int cvt_slot(int f, int ns) { return slot(NF + 1 + 3 * f + 2, ns); }
+    // The PV products of fragment f occupy slots na + f*nd .. na + f*nd + nd - 1.
+    __host__ __device__ static constexpr bool packed_in_time(int na, int nd, int ns) {
+        for (int f = 0; f < NF; ++f)
+            if (cvt_slot(f, ns) >= na + f * nd) return false;
+        return true;
+    }
+};
+
+template <int D, int BC, int NSTAGE, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArgs a) {
+    constexpr int QW = 32, BR = QW * NW, NKB = BC / 32;
     using C = Cfg<D, BC, 32, NW>;
     using acc_t = f32x16_t;
     constexpr int NQK = C::NQK, ND = C::ND;
@@ -39,8 +95,15 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf1
     static_assert(C::NCOPY % NW == 0, "copies must split evenly over the waves");
     constexpr int P = NSTAGE - 1;          // copies run P tiles ahead
     static_assert(P >= 1 && P <= 3, "2..4 stages");
-    constexpr int QK_MFMA = NKB * NQK * QB;     // per tile
-    constexpr int PV_MFMA = NKB * 2 * ND * QB;  // per tile
+    constexpr int NA = NKB * NQK;          // QK products per tile
+    constexpr int NB = NKB * 2 * ND;       // PV products per tile
+    constexpr int NS = NA + NB;            // matrix-core slots per step
+    constexpr int NF = 2 * NKB;            // 8-score P fragments per tile
+    constexpr int LA = 3;                  // K fragment reads run LA slots ahead
+    constexpr int LB = 2;                  // V fragment reads run LB slots ahead
+    using Plan = ChunkPlan<NF>;
+    // PV product pv uses fragment pv / ND; its packing must come earlier.
+    static_assert(Plan::packed_in_time(NA, ND, NS), "every P fragment packed before its PV product");
 
     // One LDS array per K stage and per V stage.
     __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[C::TILE];
@@ -138,17 +201,16 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf1
     // Q fragments (B operand of S^T = K Q^T), sign-folded so that c >= 0.
     const float c = scale_factor(a.scale_log2);
     const uint32_t sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-    bf16x8_t qf[QB][NQK];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wq0 + 32 * qb + lane % 32;
+    bf16x8_t qf[NQK];
+    {
+        const int qrow = wq0 + lane % 32;
 #pragma unroll
         for (int ks = 0; ks < NQK; ++ks) {
             u32x4_t x = {0u, 0u, 0u, 0u};
             if (qrow < N)
                 x = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
             x ^= sign;
-            qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
+            qf[ks] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
 
@@ -158,90 +220,64 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf1
     // (2ks + lane/32) ^ zk(r) fits in the low bits, so the element offset is
     // kbase0 ^ (16*ks): one base register instead of NQK.
     const int kbase0 = (lane % 32) * D + (((lane / 32) ^ C::zk(lane % 32)) << 3);
-    const int g = lane >> 4, li = lane & 15;
+    const int grp = lane >> 4, li = lane & 15;
     int vaddr[ND];
 #pragma unroll
     for (int mb = 0; mb < ND; ++mb) {
-        const int row = 4 * (g >> 1) + (li >> 2);
-        const int col = mb * 32 + 16 * (g & 1) + 4 * (li & 3);
+        const int row = 4 * (grp >> 1) + (li >> 2);
+        const int col = mb * 32 + 16 * (grp & 1) + 4 * (li & 3);
         vaddr[mb] = row * D + (((col >> 3) ^ C::zv(row)) << 3) + (col & 7);
     }
 
-    acc_t o[QB][ND];
+    acc_t o[ND];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int mb = 0; mb < ND; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < ND; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[qb][mb][i] = 0.f;
-    float m[QB], l[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = kNegInf;
-        l[qb] = 0.f;
-    }
+        for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
+    float m = kNegInf, l = 0.f;
     // Scores ping-pong between sA and sB across consecutive iterations.
-    acc_t sA[QB][NKB], sB[QB][NKB];
+    acc_t sA[NKB], sB[NKB];
 
-    auto qk_plain = [&](acc_t (&dst)[QB][NKB], const __bf16 *Ks) {
-        auto kaddr = [&](int ks) { return kbase0 ^ (ks << 4); };
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) dst[qb][kb][i] = 0.f;
+    auto qk_plain = [&](acc_t (&dst)[NKB], const __bf16 *Ks) {
+        const acc_t zero = {};
 #pragma unroll
         for (int ks = 0; ks < NQK; ++ks)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + kb * 32 * D + kaddr(ks));
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    dst[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], dst[qb][kb], 0, 0, 0);
+                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + kb * 32 * D + (kbase0 ^ (ks << 4)));
+                dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? zero : dst[kb], 0, 0, 0);
             }
     };
 
     // One pipeline step: softmax + PV of tile t (scores in s), and the
     // scores of the next tile (from Kn) into sn.  The QK products are issued
     // even when this wave has no next tile (the result is then unused): a
-    // branch would split the scheduling region that interleaves the pipes.
-    auto step = [&](int t, acc_t (&s)[QB][NKB], acc_t (&sn)[QB][NKB], const __bf16 *Kn,
-                    const __bf16 *Vs) {
+    // branch would split the schedule below.
+    //
+    // Schedule.  The step is a fixed sequence of NA + NB slots, one
+    // matrix-core instruction each (NA QK products of the next tile, then NB
+    // PV products of this tile), separated by sched_barrier fences so the
+    // compiler cannot regroup them.  The tile's VALU work, in dependency
+    // order (row max, rescale factor, exponentials, bf16 packing, row sum),
+    // is cut into chunks that are spread evenly over the slots
+    // (chunk_slot), so the VALU works while the matrix core runs.  LDS reads
+    // of K and V fragments are issued a few slots ahead of their products.
+    auto step = [&](int t, acc_t (&s)[NKB], acc_t (&sn)[NKB], const __bf16 *Kn, const __bf16 *Vs) {
         const int kbase = t * BC;
         const bool edge = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
         if (edge) {
             // Keep this a branch: the compiler would otherwise if-convert it
             // into per-element selects on every tile.
             asm volatile("" ::);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int qrow = wq0 + 32 * qb + lane % 32;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kbase + kb * 32 + Frag<32>::row(i, lane);
-                        const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
-                        s[qb][kb][i] = ok ? s[qb][kb][i] : kNegInf;
-                    }
-            }
-        }
-        float alpha[QB], neg_m[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = kNegInf;
+            const int qrow = wq0 + lane % 32;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-            mx = group_max<32>(mx);
-            const float m_tile = mx == kNegInf ? kNegInf : mx * c;
-            const float m_new = fmaxf(m[qb], m_tile);
-            const float m_use = m_new == kNegInf ? 0.f : m_new;
-            alpha[qb] = fast_exp2(m[qb] - m_use);
-            neg_m[qb] = -m_use;
-            m[qb] = m_new;
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kbase + kb * 32 + Frag<32>::row(i, lane);
+                    const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
+                    s[kb][i] = ok ? s[kb][i] : kNegInf;
+                }
         }
 
         // The K read offsets are rederived from kbase0 in every step (one XOR
@@ -249,86 +285,98 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf1
         // empty asm stops the compiler from hoisting them out of the loop.
         int kb0 = kbase0;
         asm volatile("" : "+v"(kb0));
-        auto kaddr = [&](int ks) { return kb0 ^ (ks << 4); };
 
-        // Phase A: QK of the next tile on the matrix cores || exponentials of
-        // this tile on the VALU (masked keys: exp2(-inf) = 0).
+        bf16x8_t kf[NA], vf[NB], pf[NF];
+        float mx = kNegInf, alpha = 1.f, neg_m = 0.f, rs = 0.f;
+        bool rescale = true;
+
+        auto kread = [&](auto A) {
+            constexpr int a = decltype(A)::value, ks = a / NKB, kb = a % NKB;
+            kf[a] = *reinterpret_cast<const bf16x8_t *>(Kn + kb * 32 * D + (kb0 ^ (ks << 4)));
+        };
+        auto vread = [&](auto PV) {
+            constexpr int pv = decltype(PV)::value, f = pv / ND, mb = pv % ND;
+            const __bf16 *vp = Vs + ((f / 2) * 32 + (f % 2) * 16) * D + vaddr[mb];
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vp + 8 * D));
+            vf[pv] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // Fragment f holds scores s[f/2][8*(f%2) .. 8*(f%2)+7] of each lane.
+        auto chunk = [&](auto K) {
+            constexpr int k = decltype(K)::value, kind = Plan::kind(k), f = Plan::frag(k);
+            constexpr int kb = f / 2, i0 = 8 * (f % 2);
+            if constexpr (kind == kChunkMax) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+                for (int j = 0; j < 8; ++j) mx = fmaxf(mx, s[kb][i0 + j]);
+                pin(mx);
+            } else if constexpr (kind == kChunkRed) {
+                mx = group_max<32>(mx);
+                const float m_tile = mx == kNegInf ? kNegInf : mx * c;
+                const float m_new = fmaxf(m, m_tile);
+                const float m_use = m_new == kNegInf ? 0.f : m_new;
+                alpha = fast_exp2(m - m_use);
+                neg_m = -m_use;
+                m = m_new;
+                // O needs rescaling only when some row's maximum moved
+                // (alpha = 1 exactly otherwise).
+                rescale = wave_any(alpha != 1.f);
+                pin(alpha);
+                pin(neg_m);
+            } else if constexpr (kind == kChunkExp) {
+                constexpr int j0 = i0 + 4 * Plan::half(k);
+                float e[4];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                for (int j = 0; j < 4; ++j) e[j] = fast_exp2(fmaf(s[kb][j0 + j], c, neg_m));
+                pin4(e[0], e[1], e[2], e[3]);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sn[qb][kb][i] = 0.f;
-        constexpr int PER = 16 * NKB * QB / QK_MFMA;  // exponentials per QK instruction
-        int e_next = 0;
+                for (int j = 0; j < 4; ++j) s[kb][j0 + j] = e[j];
+            } else if constexpr (kind == kChunkCvt) {
 #pragma unroll
-        for (int ks = 0; ks < NQK; ++ks)
+                for (int j = 0; j < 8; ++j) pf[f][j] = (__bf16)s[kb][i0 + j];
+                pin(pf[f]);
+            } else {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Kn + kb * 32 * D + kaddr(ks));
+                for (int j = 0; j < 8; ++j) rs += s[kb][i0 + j];
+                pin(rs);
+            }
+        };
+
+        static_for<NS>([&](auto G) {
+            constexpr int g = decltype(G)::value;
+            if constexpr (g == 0) static_for<(LA < NA ? LA : NA)>([&](auto A) { kread(A); });
+            if constexpr (g < NA && g + LA < NA) kread(IntTag<g + LA>{});
+            static_for<NB>([&](auto PV) {
+                if constexpr (vread_slot_of(decltype(PV)::value, NA, LB) == g) vread(PV);
+            });
+            if constexpr (g < NA) {
+                constexpr int ks = g / NKB, kb = g % NKB;
+                if constexpr (ks == 0) {
+                    const acc_t zero = {};
+                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g], qf[ks], zero, 0, 0, 0);
+                } else {
+                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g], qf[ks], sn[kb], 0, 0, 0);
+                }
+            } else {
+                constexpr int pv = g - NA, f = pv / ND, mb = pv % ND;
+                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[pv], pf[f], o[mb], 0, 0, 0);
+            }
+            static_for<Plan::NCH>([&](auto K) {
+                if constexpr (Plan::slot(decltype(K)::value, NS) == g) chunk(K);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (g == NA - 1) {
+                if (rescale) {
+                    // Between the phases: the first PV product of every
+                    // output block follows.  A wave-uniform branch.
+                    asm volatile("" ::);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    sn[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], sn[qb][kb], 0, 0, 0);
+                    for (int mb = 0; mb < ND; ++mb)
 #pragma unroll
-                    for (int e = 0; e < PER; ++e, ++e_next) {
-                        const int eq = e_next / (16 * NKB), ek = (e_next / 16) % NKB, ei = e_next & 15;
-                        s[eq][ek][ei] = fast_exp2(fmaf(s[eq][ek][ei], c, neg_m[eq]));
-                    }
+                        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
                 }
             }
-        // K reads run ahead of their products.
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-#pragma unroll
-        for (int i = 0; i < QK_MFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            if (i % QB == 0 && i / QB + 2 < NKB * NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgValu, 2 * PER, 0);
-        }
-
-        // Phase B: O^T = alpha*O^T + V^T P^T on the matrix cores || row sum,
-        // bf16 packing and the rescale on the VALU.
-        float rs[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bf16x8_t pf[QB];
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        pf[qb][j] = (__bf16)s[qb][kb][8 * h + j];
-                        rs[qb] += s[qb][kb][8 * h + j];
-                    }
-#pragma unroll
-                for (int mb = 0; mb < ND; ++mb) {
-                    const __bf16 *vp = Vs + (kb * 32 + h * 16) * D + vaddr[mb];
-                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
-                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vp + 8 * D));
-                    const bf16x8_t va = __builtin_bit_cast(
-                        bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        if (kb == 0 && h == 0) {
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) o[qb][mb][i] *= alpha[qb];
-                        }
-                        o[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb], o[qb][mb], 0, 0, 0);
-                    }
-                }
-            }
-        constexpr int VALU_B = (16 * ND + 24 * NKB) * QB / PV_MFMA + 1;
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 1);
-#pragma unroll
-        for (int i = 0; i < PV_MFMA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
-            if (i % QB == 0 && i / QB + 2 < 2 * NKB * ND) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 1);
-            __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_B, 1);
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l[qb] = fmaf(l[qb], alpha[qb], rs[qb]);
+        });
+        l = fmaf(l, alpha, rs);
     };
 
     // ---- pipeline ---------------------------------------------------------
@@ -353,7 +401,7 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf1
     __syncthreads();
     if (active(tq[0])) qk_plain(sA, kstage(0));
 
-    auto iteration = [&](auto stage_tag, acc_t (&s)[QB][NKB], acc_t (&sn)[QB][NKB]) {
+    auto iteration = [&](auto stage_tag, acc_t (&s)[NKB], acc_t (&sn)[NKB]) {
         constexpr int u = decltype(stage_tag)::value;  // i % NSTAGE
         const int t_new = next_tile(tq[P] + 1);         // T[i+P+1]
         // Copies younger than those of K(T[i+1]) and V(T[i]) were issued in
@@ -392,10 +440,9 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf1
     }
 
     // Epilogue: normalise, round to bf16 once, write O and LSE.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wq0 + 32 * qb + lane % 32;
-        const float l_tot = group_sum<32>(l[qb]);
+    {
+        const int qrow = wq0 + lane % 32;
+        const float l_tot = group_sum<32>(l);
         if (qrow < N) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             __bf16 *orow = O + (int64_t)qrow * D;
@@ -405,36 +452,36 @@ __global__ __launch_bounds__(NW * 64, (QB == 1 && NW == 4) ? 2 : 1) void fwd_bf1
                 for (int gg = 0; gg < 4; ++gg) {
                     bf16x4_t w;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[qb][mb][4 * gg + j] * inv);
+                    for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[mb][4 * gg + j] * inv);
                     *reinterpret_cast<bf16x4_t *>(orow + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
                 }
             if (a.lse && lane < 32)
-                a.lse[(int64_t)bh * N + qrow] = l_tot > 0.f ? (m[qb] + fast_log2(l_tot)) * kLn2 : kNegInf;
+                a.lse[(int64_t)bh * N + qrow] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
         }
     }
 }
 
-template <int D, int QB, int BC, int NSTAGE, int NW, bool CAUSAL>
+template <int D, int BC, int NSTAGE, int NW, bool CAUSAL>
 hipError_t launch_pipe(const FwdArgs &a, hipStream_t stream) {
-    constexpr int BR = 32 * QB * NW;
+    constexpr int BR = 32 * NW;
     const int nqt = (a.N + BR - 1) / BR;
-    hipLaunchKernelGGL((fwd_bf16_pipe<D, QB, BC, NSTAGE, NW, CAUSAL>),
+    hipLaunchKernelGGL((fwd_bf16_pipe<D, BC, NSTAGE, NW, CAUSAL>),
                        dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-#define FA_PIPE(D, QB, BC, NS, NW) \
-    Instance{D, 0, 32 * QB * NW, BC, &launch_pipe<D, QB, BC, NS, NW, false>}, \
-    Instance{D, 1, 32 * QB * NW, BC, &launch_pipe<D, QB, BC, NS, NW, true>}
+#define FA_PIPE(D, BC, NS, NW) \
+    Instance{D, 0, 32 * NW, BC, &launch_pipe<D, BC, NS, NW, false>}, \
+    Instance{D, 1, 32 * NW, BC, &launch_pipe<D, BC, NS, NW, true>}
 
 }  // namespace
 
 const Instance *bf16_tuned_instances() {
     static const Instance table[] = {
-        FA_PIPE(64, 1, 64, 2, 4),
-        FA_PIPE(64, 1, 64, 2, 8),
-        FA_PIPE(128, 1, 64, 2, 4),
-        FA_PIPE(128, 1, 64, 2, 8),
+        FA_PIPE(64, 64, 2, 4),
+        FA_PIPE(64, 64, 2, 8),
+        FA_PIPE(128, 64, 2, 4),
+        FA_PIPE(128, 64, 2, 8),
         Instance{0, 0, 0, 0, nullptr},
     };
     return table;
