@@ -65,7 +65,8 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL_PTR = 1,             /* q, k, v or o is NULL                        */
-    FA_ERR_INVALID_SHAPE = 2,        /* B, H or N < 1, or the grid would overflow   */
+    FA_ERR_INVALID_SHAPE = 2,        /* B, H, H_kv or N < 1, H % H_kv != 0, or the
+                                        grid would overflow                         */
     FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {64, 128}                          */
     FA_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte, lse/key_len not 4-byte */
     FA_ERR_UNSUPPORTED_TILE = 5,     /* (Br, Bc) pair or dtype not built            */
@@ -114,6 +115,24 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N, int d, float scale, int causal,
               const int32_t *key_len, const uint8_t *block_mask,
               hipStream_t stream, int dtype, int Br, int Bc);
+
+/*
+ * Grouped-query attention: the H query heads of each batch entry are split
+ * into H_kv consecutive groups of H / H_kv heads, and every head of group g
+ * attends to key/value head g (H_kv = H: plain multi-head attention;
+ * H_kv = 1: multi-query attention).  This is the head sharing that the page
+ * on FlashAttention-2 adoption (tcdigital.jp, section on the synergy with
+ * MQA/GQA) says the method combines with.  Same arguments as fa_fwd_ex
+ * except:
+ *   k, v : DEVICE pointers, contiguous [B, H_kv, N, d] (16-byte aligned)
+ *   H_kv : key/value heads, >= 1, H must be a multiple of H_kv
+ *          (else FA_ERR_INVALID_SHAPE).
+ * q, o, lse keep their [B, H, ...] layouts; o must not overlap q, k or v.
+ */
+int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int H, int H_kv, int N, int d, float scale, int causal,
+               const int32_t *key_len, const uint8_t *block_mask,
+               hipStream_t stream, int dtype, int Br, int Bc);
 
 /* Query rows (Br) and key rows (Bc) per tile that fa_fwd_ex would use for
  * (dtype, d, block mask given or not, Br, Bc); writes them to *br_out /

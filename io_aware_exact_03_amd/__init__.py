@@ -1,7 +1,7 @@
 """Python binding of the gfx950 exact-attention forward library (libfa.so).
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
-``fa_fwd_ex``, ``fa_tile_shape``, ``fa_status_string``,
+``fa_fwd_ex``, ``fa_fwd_gqa``, ``fa_tile_shape``, ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
 the library's HIP kernels.  ``fwd`` is a convenience wrapper that allocates
@@ -12,7 +12,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_tile_shape",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_gqa", "fa_tile_shape",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
            "DTYPE_BF16", "DTYPE_F32", "MASK_BLOCK"]
 
@@ -59,6 +59,8 @@ def _load():
     lib.fa_fwd_f32.restype = i32
     lib.fa_fwd_ex.argtypes = fwd_args + [i32, i32, i32]
     lib.fa_fwd_ex.restype = i32
+    lib.fa_fwd_gqa.argtypes = fwd_args[:7] + [i32] + fwd_args[7:] + [i32, i32, i32]
+    lib.fa_fwd_gqa.restype = i32
     lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fa_tile_shape.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -95,6 +97,12 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, s
                              key_len, block_mask, stream, dtype, Br, Bc), "fa_fwd_ex")
 
 
+def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
+               dtype, Br, Bc):
+    _check(_load().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, int(bool(causal)),
+                              key_len, block_mask, stream, dtype, Br, Bc), "fa_fwd_gqa")
+
+
 def fa_tile_shape(dtype, d, block_sparse=False, Br=0, Bc=0):
     br, bc = ctypes.c_int(0), ctypes.c_int(0)
     _check(_load().fa_tile_shape(dtype, d, int(bool(block_sparse)), Br, Bc, ctypes.byref(br),
@@ -117,7 +125,9 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
         out=None, lse=None, stream=None):
     """Attention forward on device tensors.
 
-    q, k, v: contiguous [B, H, N, d] cuda tensors, all bfloat16 or all float32.
+    q: contiguous [B, H, N, d] cuda tensor, bfloat16 or float32; k, v: the
+    same dtype, [B, H_kv, N, d] with H a multiple of H_kv (H_kv < H runs
+    grouped-query attention through fa_fwd_gqa).
     key_len: int32 cuda tensor [B] or None.  block_mask: uint8 cuda tensor with
     ceil(N/128)^2 entries (row = query block) or None.  scale defaults to
     1/sqrt(d).  Br/Bc = 0 selects the tuned tile.  Returns (o, lse) with o like
@@ -136,9 +146,10 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
             raise ValueError(f"{name} must be a contiguous 4-d cuda tensor")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k and v must share the shape [B, H, N, d]")
     B, H, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k and v must have the shape [B, H_kv, N, d] of q's B, N, d")
+    H_kv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -159,7 +170,12 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
         bm_ptr = block_mask.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-              lse.data_ptr() if want_lse else None, B, H, N, d, float(scale),
-              causal, kl_ptr, bm_ptr, stream, dtype, Br, Bc)
+    if H_kv == H:
+        fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                  lse.data_ptr() if want_lse else None, B, H, N, d, float(scale),
+                  causal, kl_ptr, bm_ptr, stream, dtype, Br, Bc)
+    else:
+        fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                   lse.data_ptr() if want_lse else None, B, H, H_kv, N, d, float(scale),
+                   causal, kl_ptr, bm_ptr, stream, dtype, Br, Bc)
     return out, (lse if want_lse else None)

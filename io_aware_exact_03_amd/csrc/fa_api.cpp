@@ -53,11 +53,11 @@ int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
     return FA_OK;
 }
 
-int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
-            int d, float scale, int causal, const int32_t *key_len, const uint8_t *block_mask,
-            hipStream_t stream, int dtype, int br, int bc) {
+int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+            int Hkv, int N, int d, float scale, int causal, const int32_t *key_len,
+            const uint8_t *block_mask, hipStream_t stream, int dtype, int br, int bc) {
     if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
-    if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_SHAPE;
+    if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED_TILE;
     // Grid size limit: B*H*ceil(N/16) workgroups at the smallest tile.
@@ -69,7 +69,8 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
     const uint64_t elem = dtype == FA_DTYPE_BF16 ? 2 : 4;
     const uint64_t bytes = (uint64_t)B * H * N * d * elem;
-    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    const uint64_t kv_bytes = (uint64_t)B * Hkv * N * d * elem;
+    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, kv_bytes) || overlaps(o, bytes, v, kv_bytes))
         return FA_ERR_INVALID_ARG;
     const uint64_t lse_bytes = (uint64_t)B * H * N * sizeof(float);
     if (lse && overlaps(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
@@ -90,6 +91,8 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     a.B = B;
     a.H = H;
     a.N = N;
+    a.Hkv = Hkv;
+    a.group = H / Hkv;
     a.nkb = (N + 127) / 128;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
@@ -108,22 +111,29 @@ extern "C" {
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
            int d, float scale, int causal, const int32_t *key_len, const uint8_t *block_mask,
            hipStream_t stream) {
-    return forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream,
+    return forward(q, k, v, o, lse, B, H, H, N, d, scale, causal, key_len, block_mask, stream,
                    FA_DTYPE_BF16, 0, 0);
 }
 
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B, int H,
                int N, int d, float scale, int causal, const int32_t *key_len,
                const uint8_t *block_mask, hipStream_t stream) {
-    return forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream,
+    return forward(q, k, v, o, lse, B, H, H, N, d, scale, causal, key_len, block_mask, stream,
                    FA_DTYPE_F32, 0, 0);
 }
 
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
               int N, int d, float scale, int causal, const int32_t *key_len,
               const uint8_t *block_mask, hipStream_t stream, int dtype, int Br, int Bc) {
-    return forward(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream, dtype,
+    return forward(q, k, v, o, lse, B, H, H, N, d, scale, causal, key_len, block_mask, stream, dtype,
                    Br, Bc);
+}
+
+int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+               int H_kv, int N, int d, float scale, int causal, const int32_t *key_len,
+               const uint8_t *block_mask, hipStream_t stream, int dtype, int Br, int Bc) {
+    return forward(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
+                   dtype, Br, Bc);
 }
 
 int fa_tile_shape(int dtype, int d, int block_sparse, int Br, int Bc, int *br_out, int *bc_out) {
@@ -135,7 +145,8 @@ const char *fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULL_PTR: return "null pointer argument";
-        case FA_ERR_INVALID_SHAPE: return "invalid shape (B, H, N must be >= 1 and the grid must fit)";
+        case FA_ERR_INVALID_SHAPE:
+            return "invalid shape (B, H, H_kv, N must be >= 1, H a multiple of H_kv, and the grid must fit)";
         case FA_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (d must be 64 or 128)";
         case FA_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 bytes, lse/key_len 4)";
         case FA_ERR_UNSUPPORTED_TILE: return "unsupported dtype or tile shape";

@@ -65,6 +65,14 @@ __device__ __forceinline__ bool wave_any(bool pred) {
     return __builtin_amdgcn_ballot_w64(pred) != 0;
 }
 
+// Key/value head read by query head bh = b*H + h: consecutive groups of
+// H/Hkv query heads share one key/value head (grouped-query attention;
+// Hkv = H is plain multi-head attention, Hkv = 1 multi-query attention).
+__device__ __forceinline__ int kv_head_of(int bh, const FwdArgs &a) {
+    const int b = bh / a.H;
+    return b * a.Hkv + (bh - b * a.H) / a.group;
+}
+
 // Workgroup -> (head, query tile) order.  Workgroups are handed to the eight
 // XCDs round-robin; when the grid divides evenly, renumber so that each XCD
 // receives one contiguous run of logical tiles (whole heads where possible),

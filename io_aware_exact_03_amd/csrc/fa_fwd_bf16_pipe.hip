@@ -124,9 +124,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
     tile_of_block(nqt, CAUSAL, &bh, &qt);
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
+    const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
     const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
-    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + head;
-    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + head;
+    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + kvhead;
+    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + kvhead;
     __bf16 *O = reinterpret_cast<__bf16 *>(a.o) + head;
 
     const int q0 = qt * BR;

@@ -32,9 +32,10 @@ __global__ __launch_bounds__(kNwF32 * 64) void fwd_f32_kernel(FwdArgs a) {
     tile_of_block(nqt, CAUSAL, &bh, &qt);
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
+    const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
     const float *Q = reinterpret_cast<const float *>(a.q) + head;
-    const float *K = reinterpret_cast<const float *>(a.k) + head;
-    const float *V = reinterpret_cast<const float *>(a.v) + head;
+    const float *K = reinterpret_cast<const float *>(a.k) + kvhead;
+    const float *V = reinterpret_cast<const float *>(a.v) + kvhead;
     float *O = reinterpret_cast<float *>(a.o) + head;
 
     const int q0 = qt * BR, wq0 = q0 + wave * 32, qrow = wq0 + lane % 32;

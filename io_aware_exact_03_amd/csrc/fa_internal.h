@@ -17,6 +17,8 @@ struct FwdArgs {
     const int32_t *key_len;     // may be null
     const uint8_t *block_mask;  // may be null; ceil(N/128)^2 bytes
     int B, H, N;
+    int Hkv;                    // key/value heads (H for plain multi-head attention)
+    int group;                  // H / Hkv query heads per key/value head
     int nkb;                    // ceil(N/128): row length of block_mask
     float scale_log2;           // softmax scale * log2(e), fp32
 };

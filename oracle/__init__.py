@@ -33,11 +33,20 @@ def _configure(lib):
                                  ctypes.c_double, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_void_p, i64]
     lib.attn_ref_f64.restype = ctypes.c_int
+    lib.attn_ref_gqa_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                     ctypes.c_double, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p, i64]
+    lib.attn_ref_gqa_f64.restype = ctypes.c_int
     lib.attn_ref_rows_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64,
                                       ctypes.c_double, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, i64,
                                       ctypes.c_void_p, i64, dp, dp]
     lib.attn_ref_rows_f64.restype = ctypes.c_int
+    lib.attn_ref_rows_gqa_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64,
+                                          ctypes.c_double, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p, i64,
+                                          ctypes.c_void_p, i64, dp, dp]
+    lib.attn_ref_rows_gqa_f64.restype = ctypes.c_int
     lib.attn_ref_threads.restype = ctypes.c_int
     return lib
 
@@ -63,9 +72,11 @@ def _ptr(a):
 
 def _prep(q, k, v, key_len, block_mask, block):
     q, k, v = _f64(q), _f64(k), _f64(v)
-    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share the shape [B, H, N, d]")
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, H_kv, N, d]")
     B, H, N, d = q.shape
+    if k.shape[0] != B or k.shape[2:] != (N, d) or k.shape[1] < 1 or H % k.shape[1]:
+        raise ValueError("k, v must be [B, H_kv, N, d] with H a multiple of H_kv")
     kl = None
     if key_len is not None:
         kl = np.ascontiguousarray(key_len, dtype=np.int32)
@@ -85,13 +96,15 @@ def attention_f64(q, k, v, scale, causal=False, key_len=None, block_mask=None,
     """O [B,H,N,d] float64 and LSE [B,H,N] float64 for the whole problem.
 
     ``scale`` is used as given (pass the same float32 value the GPU gets).
+    k, v may have H_kv < H heads (grouped-query attention: query head h of a
+    batch entry reads key/value head h // (H // H_kv)).
     """
     q, k, v, kl, bm = _prep(q, k, v, key_len, block_mask, block)
     B, H, N, d = q.shape
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
-    rc = _load().attn_ref_f64(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+    rc = _load().attn_ref_gqa_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, k.shape[1], N, d,
         float(scale), int(bool(causal)),
         kl.ctypes.data if kl is not None else None,
         bm.ctypes.data if bm is not None else None, block)
@@ -112,8 +125,8 @@ def attention_rows_f64(q, k, v, rows, scale, causal=False, key_len=None,
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
     o = np.empty((rows.size, d), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64)
-    rc = _load().attn_ref_rows_f64(
-        _ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(bool(causal)),
+    rc = _load().attn_ref_rows_gqa_f64(
+        _ptr(q), _ptr(k), _ptr(v), B, H, k.shape[1], N, d, float(scale), int(bool(causal)),
         kl.ctypes.data if kl is not None else None,
         bm.ctypes.data if bm is not None else None, block,
         rows.ctypes.data, rows.size, _ptr(o), _ptr(lse))

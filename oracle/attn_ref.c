@@ -32,7 +32,8 @@
  * unchanged) so that large logits do not overflow.
  * LSE_i = log(sum_j exp(S_ij)) in natural log.
  *
- * Layout: q, k, v, o are contiguous [B, H, N, d]; lse is [B, H, N].
+ * Layout: q, o are contiguous [B, H, N, d]; k, v are [B, H, N, d] (or
+ * [B, Hkv, N, d] for the grouped-query entry points); lse is [B, H, N].
  * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/build.py).
  */
 #include <math.h>
@@ -96,24 +97,35 @@ static void score_row(double *s, const double *qi, const double *kh, int64_t i,
 }
 
 static int check_args(const double *q, const double *k, const double *v,
-                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
                       const uint8_t *block_mask, int64_t blk)
 {
     if (!q || !k || !v) return 1;
     if (B < 0 || H < 0 || N < 0 || d <= 0) return 2;
+    if (Hkv <= 0 || H % Hkv != 0) return 2;
     if (block_mask && blk <= 0) return 2;
     return 0;
+}
+
+/* Key/value head used by query head h of batch entry b when the H query
+ * heads share Hkv key/value heads in consecutive groups of H / Hkv
+ * (grouped-query attention, on the page on FlashAttention-2 adoption,
+ * tcdigital.jp, section on the synergy with MQA/GQA; Hkv = H is plain
+ * multi-head attention).  k and v are [B, Hkv, N, d]. */
+static int64_t kv_head(int64_t b, int64_t h, int64_t H, int64_t Hkv)
+{
+    return b * Hkv + h / (H / Hkv);
 }
 
 /* Full evaluation: every (b, h) head, S materialised as an N x N array of
  * doubles one head at a time (A overwrites S in place).  Returns 0 on success,
  * non-zero on bad arguments or allocation failure. */
-int attn_ref_f64(const double *q, const double *k, const double *v, double *o,
-                 double *lse, int64_t B, int64_t H, int64_t N, int64_t d,
-                 double scale, int causal, const int32_t *key_len,
-                 const uint8_t *block_mask, int64_t blk)
+int attn_ref_gqa_f64(const double *q, const double *k, const double *v, double *o,
+                     double *lse, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                     int64_t d, double scale, int causal, const int32_t *key_len,
+                     const uint8_t *block_mask, int64_t blk)
 {
-    int rc = check_args(q, k, v, B, H, N, d, block_mask, blk);
+    int rc = check_args(q, k, v, B, H, Hkv, N, d, block_mask, blk);
     if (rc) return rc;
     if (!o || !lse) return 1;
     if (N == 0) return 0;
@@ -122,8 +134,8 @@ int attn_ref_f64(const double *q, const double *k, const double *v, double *o,
     if (!S) return 3;
     for (int64_t b = 0; b < B; ++b) {
         for (int64_t h = 0; h < H; ++h) {
-            const int64_t head = (b * H + h) * N;
-            const double *qh = q + head * d, *kh = k + head * d, *vh = v + head * d;
+            const int64_t head = (b * H + h) * N, kvh = kv_head(b, h, H, Hkv) * N;
+            const double *qh = q + head * d, *kh = k + kvh * d, *vh = v + kvh * d;
             double *oh = o + head * d, *lh = lse + head;
 #pragma omp parallel for schedule(dynamic, 16)
             for (int64_t i = 0; i < N; ++i)
@@ -138,18 +150,28 @@ int attn_ref_f64(const double *q, const double *k, const double *v, double *o,
     return 0;
 }
 
+/* Plain multi-head attention: one key/value head per query head. */
+int attn_ref_f64(const double *q, const double *k, const double *v, double *o,
+                 double *lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                 double scale, int causal, const int32_t *key_len,
+                 const uint8_t *block_mask, int64_t blk)
+{
+    return attn_ref_gqa_f64(q, k, v, o, lse, B, H, H, N, d, scale, causal,
+                            key_len, block_mask, blk);
+}
+
 /* Sampled evaluation: only the query rows listed in rows[] are computed.
  * rows[r] is a flat row index (b * H + h) * N + i.  o_rows is [n_rows, d],
  * lse_rows is [n_rows].  Each row is the same definition as above, with that
  * row of S materialised on its own. */
-int attn_ref_rows_f64(const double *q, const double *k, const double *v,
-                      int64_t B, int64_t H, int64_t N, int64_t d, double scale,
-                      int causal, const int32_t *key_len,
-                      const uint8_t *block_mask, int64_t blk,
-                      const int64_t *rows, int64_t n_rows, double *o_rows,
-                      double *lse_rows)
+int attn_ref_rows_gqa_f64(const double *q, const double *k, const double *v,
+                          int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                          double scale, int causal, const int32_t *key_len,
+                          const uint8_t *block_mask, int64_t blk,
+                          const int64_t *rows, int64_t n_rows, double *o_rows,
+                          double *lse_rows)
 {
-    int rc = check_args(q, k, v, B, H, N, d, block_mask, blk);
+    int rc = check_args(q, k, v, B, H, Hkv, N, d, block_mask, blk);
     if (rc) return rc;
     if (n_rows > 0 && (!rows || !o_rows || !lse_rows)) return 1;
     for (int64_t r = 0; r < n_rows; ++r)
@@ -169,7 +191,8 @@ int attn_ref_rows_f64(const double *q, const double *k, const double *v,
             if (!s) continue;
             const int64_t flat = rows[r];
             const int64_t head = flat / N, i = flat % N, b = head / H;
-            const double *kh = k + head * N * d, *vh = v + head * N * d;
+            const int64_t kvh = kv_head(b, head - b * H, H, Hkv);
+            const double *kh = k + kvh * N * d, *vh = v + kvh * N * d;
             score_row(s, q + flat * d, kh, i, b, N, d, scale, causal, key_len,
                       block_mask, blk, nkb);
             softmax_row_times_v(s, vh, o_rows + r * d, lse_rows + r, N, d);
@@ -177,6 +200,17 @@ int attn_ref_rows_f64(const double *q, const double *k, const double *v,
         free(s);
     }
     return failed ? 3 : 0;
+}
+
+int attn_ref_rows_f64(const double *q, const double *k, const double *v,
+                      int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                      int causal, const int32_t *key_len,
+                      const uint8_t *block_mask, int64_t blk,
+                      const int64_t *rows, int64_t n_rows, double *o_rows,
+                      double *lse_rows)
+{
+    return attn_ref_rows_gqa_f64(q, k, v, B, H, H, N, d, scale, causal, key_len,
+                                 block_mask, blk, rows, n_rows, o_rows, lse_rows);
 }
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */

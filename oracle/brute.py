@@ -19,10 +19,12 @@ DPS = 40
 
 def attention_mp(q, k, v, scale, causal=False, key_len=None, block_mask=None,
                  block=128):
-    """q, k, v: nested lists or arrays [B][H][N][d]; returns (O, LSE) as nested
+    """q: nested lists or arrays [B][H][N][d], k and v [B][H_kv][N][d] (query
+    head h reads key/value head h // (H // H_kv)); returns (O, LSE) as nested
     lists of mpmath.mpf.  block_mask is a flat sequence of ceil(N/block)^2."""
     with mpmath.workdps(DPS):
         B, H, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+        G = H // len(k[0])  # query heads per key/value head (grouped-query attention)
         nkb = (N + block - 1) // block
         sc = mpmath.mpf(float(scale))
         O, L = [], []
@@ -40,12 +42,12 @@ def attention_mp(q, k, v, scale, causal=False, key_len=None, block_mask=None,
                             continue
                         if block_mask is not None and int(block_mask[(i // block) * nkb + j // block]) == 0:
                             continue
-                        s = mpmath.fsum(mpmath.mpf(float(q[b][h][i][c])) * mpmath.mpf(float(k[b][h][j][c]))
+                        s = mpmath.fsum(mpmath.mpf(float(q[b][h][i][c])) * mpmath.mpf(float(k[b][h // G][j][c]))
                                         for c in range(d))
                         w = mpmath.exp(sc * s)
                         den += w
                         for c in range(d):
-                            num[c] += w * mpmath.mpf(float(v[b][h][j][c]))
+                            num[c] += w * mpmath.mpf(float(v[b][h // G][j][c]))
                     if den == 0:
                         Oh.append([mpmath.mpf(0)] * d)
                         Lh.append(mpmath.mpf("-inf"))

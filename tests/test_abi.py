@@ -25,8 +25,9 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_tile_shape",
-                                           "fa_status_string", "fa_last_hip_error"])
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_gqa",
+                                           "fa_tile_shape", "fa_status_string",
+                                           "fa_last_hip_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -66,6 +67,27 @@ def call(**kw):
 def test_invalid_arguments_return_status_without_launch(kw, status):
     assert call(**kw) == status
     assert fa.fa_status_string(status) not in ("", "unknown status")
+
+
+def call_gqa(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=4, H_kv=2, N=100, d=64, scale=0.125,
+                causal=0, key_len=None, block_mask=None, stream=None, dtype=0, Br=0, Bc=0)
+    args.update(kw)
+    lib = fa._load()
+    return lib.fa_fwd_gqa(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                          args["H"], args["H_kv"], args["N"], args["d"], args["scale"],
+                          args["causal"], args["key_len"], args["block_mask"], args["stream"],
+                          args["dtype"], args["Br"], args["Bc"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_kv=0), 2), (dict(H_kv=3), 2), (dict(H=4, H_kv=8), 2), (dict(H_kv=-2), 2),
+    (dict(k=None), 1), (dict(d=80), 3), (dict(v=V + 4), 4),
+    # o overlapping the (smaller) key/value tensors: [B, H_kv, N, d] bf16
+    (dict(o=K + 2 * 2 * 100 * 64 * 2 - 16), 7),
+])
+def test_gqa_invalid_arguments_return_status_without_launch(kw, status):
+    assert call_gqa(**kw) == status
 
 
 def test_status_strings_cover_every_code():

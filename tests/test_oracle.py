@@ -293,3 +293,51 @@ def test_rows_entry_matches_full_evaluation():
     orow, lrow = oracle.attention_rows_f64(q, k, v, rows, 0.2, True, kl, bm, 128)
     np.testing.assert_array_equal(orow, o.reshape(-1, 32)[rows])
     np.testing.assert_array_equal(lrow, lse.reshape(-1)[rows])
+
+
+# ---------------------------------------------------------------- grouped-query attention
+# Query heads share key/value heads in consecutive groups of H / H_kv (page on
+# FlashAttention-2 adoption, tcdigital.jp, section on the synergy with MQA/GQA).
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (6, 3), (4, 1), (3, 3)])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks"])
+def test_gqa_brute_force_tiny(H, H_kv, mode):
+    """Grouped heads against the 40-digit brute force (which maps query head h
+    to key/value head h // (H // H_kv) in its own loop)."""
+    N, d = 5, 3
+    q, _, _, rng = random_qkv(2, H, N, d, seed=300 + H + 10 * H_kv, dtype="f32")
+    _, k, v, rng = random_qkv(2, H_kv, N, d, seed=400 + H + 10 * H_kv, dtype="f32", rng=rng)
+    key_len = rng.integers(0, N, size=2, endpoint=True) if mode == "padded" else None
+    bm = (rng.random(9) < 0.6).astype(np.uint8) if mode == "blocks" else None
+    o, lse = oracle.attention_f64(q, k, v, 0.7, mode == "causal", key_len, bm, 2)
+    O, L = brute.attention_mp(q, k, v, 0.7, mode == "causal", key_len, bm, 2)
+    O, L = np.array(O, dtype=np.float64), np.array(L, dtype=np.float64)
+    np.testing.assert_allclose(o, O, rtol=0, atol=1e-13)
+    fin = np.isfinite(L)
+    np.testing.assert_allclose(lse[fin], L[fin], rtol=0, atol=1e-13)
+    assert np.all(lse[~fin] == -np.inf)
+
+
+def test_gqa_equals_multi_head_with_repeated_key_values():
+    """Each key/value head repeated over its group of consecutive query heads
+    turns the grouped problem into plain multi-head attention."""
+    B, H, H_kv, N, d = 2, 8, 2, 70, 16
+    q, _, _, rng = random_qkv(B, H, N, d, seed=31, dtype="bf16")
+    _, k, v, rng = random_qkv(B, H_kv, N, d, seed=32, dtype="bf16", rng=rng)
+    kl = np.array([50, 70], dtype=np.int32)
+    o, lse = oracle.attention_f64(q, k, v, 0.25, True, kl)
+    kr, vr = np.repeat(k, H // H_kv, axis=1), np.repeat(v, H // H_kv, axis=1)
+    o2, lse2 = oracle.attention_f64(q, kr, vr, 0.25, True, kl)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    rows = rng.choice(B * H * N, 40, replace=False)
+    orow, lrow = oracle.attention_rows_f64(q, k, v, rows, 0.25, True, kl)
+    np.testing.assert_array_equal(orow, o.reshape(-1, d)[rows])
+    np.testing.assert_array_equal(lrow, lse.reshape(-1)[rows])
+
+
+def test_gqa_rejects_bad_head_counts():
+    q, k, v, _ = random_qkv(1, 4, 8, 4, seed=5, dtype="f32")
+    with pytest.raises(ValueError):
+        oracle.attention_f64(q, k[:, :3], v[:, :3], 0.5)

@@ -30,6 +30,7 @@ MUTANTS = {
     "masked_row_unguarded": ("if (m == -INFINITY) {", "if (0) {"),
     "dot_index": ("dot += qi[c] * kj[c];", "dot += qi[c] * kj[0];"),
     "value_index": ("o[c] += s[j] * vj[c];", "o[c] += s[j] * vj[0];"),
+    "kv_heads_interleaved": ("return b * Hkv + h / (H / Hkv);", "return b * Hkv + h % Hkv;"),
 }
 
 FAST_PINS = [
@@ -38,6 +39,7 @@ FAST_PINS = [
     pins.test_fully_masked_rows,
     lambda: pins.test_identity_values_expose_attention_matrix("blocks"),
     lambda: pins.test_identity_values_expose_attention_matrix("padded"),
+    pins.test_gqa_equals_multi_head_with_repeated_key_values,
 ]
 
 
