@@ -74,8 +74,12 @@ typedef enum {
     FA_ERR_INVALID_ARG = 7           /* non-finite scale, o overlapping an input    */
 } fa_status;
 
-/* Element type codes for fa_fwd_ex. */
-enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1 };
+/* Element type codes for fa_fwd_ex and fa_fwd_gqa.  FA_DTYPE_F16 (IEEE
+ * half inputs and output, fp16 probabilities as the PV operand, fp32
+ * arithmetic otherwise) is the other 16-bit format the page on
+ * FlashAttention-2 adoption (tcdigital.jp, section on fp16/bf16 precision
+ * support) names as the precisions the method is meant to run in. */
+enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1, FA_DTYPE_F16 = 2 };
 
 /*
  * bf16 inputs and output (q, k, v, o point to bfloat16), fp32 arithmetic
@@ -103,13 +107,15 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
  * Attention Stable?" explainer (aibr.jp, sections 3 and 4: block sizes Br and
  * Bc varied, output compared with an FP64 golden value).  Same arguments as
  * fa_fwd plus:
- *   dtype : FA_DTYPE_BF16 (q/k/v/o bfloat16) or FA_DTYPE_F32 (float)
+ *   dtype : FA_DTYPE_BF16 (q/k/v/o bfloat16), FA_DTYPE_F16 (IEEE half) or
+ *           FA_DTYPE_F32 (float)
  *   Br    : query rows per tile;  Bc : key rows per tile.
  * Br = Bc = 0 selects the tuned default (what fa_fwd / fa_fwd_f32 use).  For
  * bf16 every Br, Bc in {16, 32, 64, 128} is built for d = 128 (one
  * tile-study kernel family), and the tuned shapes (Br, Bc) = (128, 64) and
- * (256, 64) for d = 64 and 128; (256, 64) does not take a block mask.  fp32
- * builds only its default.  Unbuilt pairs return FA_ERR_UNSUPPORTED_TILE.
+ * (256, 64) for d = 64 and 128; (256, 64) does not take a block mask.  fp16
+ * builds (128, 64) for d = 64 and 128, fp32 only its default.  Unbuilt pairs
+ * return FA_ERR_UNSUPPORTED_TILE.
  */
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N, int d, float scale, int causal,

@@ -14,11 +14,12 @@ import os
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_gqa", "fa_tile_shape",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
-           "DTYPE_BF16", "DTYPE_F32", "MASK_BLOCK"]
+           "DTYPE_BF16", "DTYPE_F32", "DTYPE_F16", "MASK_BLOCK"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
+DTYPE_F16 = 2
 MASK_BLOCK = 128
 
 FA_OK = 0
@@ -125,7 +126,7 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
         out=None, lse=None, stream=None):
     """Attention forward on device tensors.
 
-    q: contiguous [B, H, N, d] cuda tensor, bfloat16 or float32; k, v: the
+    q: contiguous [B, H, N, d] cuda tensor, bfloat16, float16 or float32; k, v: the
     same dtype, [B, H_kv, N, d] with H a multiple of H_kv (H_kv < H runs
     grouped-query attention through fa_fwd_gqa).
     key_len: int32 cuda tensor [B] or None.  block_mask: uint8 cuda tensor with
@@ -141,6 +142,8 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
         dtype = DTYPE_BF16
     elif q.dtype == torch.float32:
         dtype = DTYPE_F32
+    elif q.dtype == torch.float16:
+        dtype = DTYPE_F16
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
     for name, t in (("q", q), ("k", k), ("v", v)):

@@ -33,12 +33,16 @@ const fa::Instance *find(const fa::Instance *table, int d, int causal, int br, i
 // one 128-token mask block do not take a block mask.
 int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
                  const fa::Instance **out, int *br_out, int *bc_out) {
-    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED_TILE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16)
+        return FA_ERR_UNSUPPORTED_TILE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     const fa::Instance *inst = nullptr;
     if (dtype == FA_DTYPE_F32) {
         if (br == 0 && bc == 0) fa::f32_default_tile(d, &br, &bc);
         inst = find(fa::f32_instances(), d, causal, br, bc);
+    } else if (dtype == FA_DTYPE_F16) {
+        if (br == 0 && bc == 0) fa::bf16_default_tile(d, block_sparse, &br, &bc);
+        inst = find(fa::f16_tuned_instances(), d, causal, br, bc);
     } else if (br == 0 && bc == 0) {
         fa::bf16_default_tile(d, block_sparse, &br, &bc);
         inst = find(fa::bf16_tuned_instances(), d, causal, br, bc);
@@ -59,7 +63,8 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
     if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED_TILE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16)
+        return FA_ERR_UNSUPPORTED_TILE;
     // Grid size limit: B*H*ceil(N/16) workgroups at the smallest tile.
     const uint64_t groups = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 15) / 16);
     if (groups >= (1ull << 31)) return FA_ERR_INVALID_SHAPE;
@@ -67,7 +72,7 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
         return FA_ERR_MISALIGNED;
     if ((lse && !aligned(lse, 4)) || (key_len && !aligned(key_len, 4))) return FA_ERR_MISALIGNED;
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-    const uint64_t elem = dtype == FA_DTYPE_BF16 ? 2 : 4;
+    const uint64_t elem = dtype == FA_DTYPE_F32 ? 4 : 2;
     const uint64_t bytes = (uint64_t)B * H * N * d * elem;
     const uint64_t kv_bytes = (uint64_t)B * Hkv * N * d * elem;
     if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, kv_bytes) || overlaps(o, bytes, v, kv_bytes))

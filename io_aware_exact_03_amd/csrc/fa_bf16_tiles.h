@@ -1,4 +1,4 @@
-// Building blocks shared by the bf16 forward kernels (gfx950): matrix-core
+// Building blocks shared by the 16-bit forward kernels (gfx950): matrix-core
 // fragment shapes, tile geometry, LDS swizzles, HBM->LDS tile copies and the
 // transposed V read.  Internal header.
 #pragma once
@@ -12,6 +12,30 @@ namespace {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+// 16-bit element types of the kernels: bf16 (the default) and fp16, with
+// their 8- and 4-wide vectors and the 32x32x16 matrix-core product
+// (fp32 accumulation) on them.
+template <class T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+    using x8 = bf16x8_t;
+    using x4 = bf16x4_t;
+    __device__ static f32x16_t mfma(x8 a, x8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Elem<_Float16> {
+    using x8 = f16x8_t;
+    using x4 = f16x4_t;
+    __device__ static f32x16_t mfma(x8 a, x8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 // ----------------------------------------------------------------------------
 // Matrix-core fragment shapes.

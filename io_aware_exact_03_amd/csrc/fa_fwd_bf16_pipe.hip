@@ -1,4 +1,5 @@
-// Tuned exact-attention forward for gfx950 (bf16 in/out, fp32 accumulation).
+// Tuned exact-attention forward for gfx950 (bf16 or fp16 in/out, fp32
+// accumulation).
 //
 // Same method and running-statistics recurrence as the tile-study kernel in
 // fa_fwd_bf16.hip (tiled exact attention with an online softmax: page
@@ -85,8 +86,11 @@ struct ChunkPlan {
     }
 };
 
-template <int D, int BC, int NSTAGE, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArgs a) {
+template <class T, int D, int BC, int NSTAGE, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) {
+    using E = Elem<T>;
+    using x8_t = typename E::x8;
+    using x4_t = typename E::x4;
     constexpr int QW = 32, BR = QW * NW, NKB = BC / 32;
     using C = Cfg<D, BC, 32, NW>;
     using acc_t = f32x16_t;
@@ -106,14 +110,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
     static_assert(Plan::packed_in_time(NA, ND, NS), "every P fragment packed before its PV product");
 
     // One LDS array per K stage and per V stage.
-    __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 k_lds2[NSTAGE > 2 ? C::TILE : 1];
-    __shared__ __attribute__((aligned(1024))) __bf16 k_lds3[NSTAGE > 3 ? C::TILE : 1];
-    __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 v_lds2[NSTAGE > 2 ? C::TILE : 1];
-    __shared__ __attribute__((aligned(1024))) __bf16 v_lds3[NSTAGE > 3 ? C::TILE : 1];
+    __shared__ __attribute__((aligned(1024))) T k_lds0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T k_lds1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T k_lds2[NSTAGE > 2 ? C::TILE : 1];
+    __shared__ __attribute__((aligned(1024))) T k_lds3[NSTAGE > 3 ? C::TILE : 1];
+    __shared__ __attribute__((aligned(1024))) T v_lds0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T v_lds1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) T v_lds2[NSTAGE > 2 ? C::TILE : 1];
+    __shared__ __attribute__((aligned(1024))) T v_lds3[NSTAGE > 3 ? C::TILE : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -125,10 +129,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
-    const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
-    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + kvhead;
-    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + kvhead;
-    __bf16 *O = reinterpret_cast<__bf16 *>(a.o) + head;
+    const T *Q = reinterpret_cast<const T *>(a.q) + head;
+    const T *K = reinterpret_cast<const T *>(a.k) + kvhead;
+    const T *V = reinterpret_cast<const T *>(a.v) + kvhead;
+    T *O = reinterpret_cast<T *>(a.o) + head;
 
     const int q0 = qt * BR;
     const int wq0 = q0 + wave * QW;
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
         koff[i] = (uint32_t)(r * D + ((p ^ C::zk(r)) << 3)) * 2u;
         voff[i] = (uint32_t)(r * D + ((p ^ C::zv(r)) << 3)) * 2u;
     }
-    auto copy = [&](const __bf16 *G, __bf16 *dst, const uint32_t(&off)[ROUNDS], int t) {
+    auto copy = [&](const T *G, T *dst, const uint32_t(&off)[ROUNDS], int t) {
         const int kbase = t * BC;
         const char *base = reinterpret_cast<const char *>(G + (int64_t)kbase * D);
         if (kbase + BC <= kv_len) {
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
     // Q fragments (B operand of S^T = K Q^T), sign-folded so that c >= 0.
     const float c = scale_factor(a.scale_log2);
     const uint32_t sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-    bf16x8_t qf[NQK];
+    x8_t qf[NQK];
     {
         const int qrow = wq0 + lane % 32;
 #pragma unroll
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
             if (qrow < N)
                 x = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
             x ^= sign;
-            qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+            qf[ks] = __builtin_bit_cast(x8_t, x);
         }
     }
 
@@ -239,14 +243,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
     // Scores ping-pong between sA and sB across consecutive iterations.
     acc_t sA[NKB], sB[NKB];
 
-    auto qk_plain = [&](acc_t (&dst)[NKB], const __bf16 *Ks) {
+    auto qk_plain = [&](acc_t (&dst)[NKB], const T *Ks) {
         const acc_t zero = {};
 #pragma unroll
         for (int ks = 0; ks < NQK; ++ks)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + kb * 32 * D + (kbase0 ^ (ks << 4)));
-                dst[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? zero : dst[kb], 0, 0, 0);
+                const x8_t ka = *reinterpret_cast<const x8_t *>(Ks + kb * 32 * D + (kbase0 ^ (ks << 4)));
+                dst[kb] = E::mfma(ka, qf[ks], ks == 0 ? zero : dst[kb]);
             }
     };
 
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
     // is cut into chunks that are spread evenly over the slots
     // (chunk_slot), so the VALU works while the matrix core runs.  LDS reads
     // of K and V fragments are issued a few slots ahead of their products.
-    auto step = [&](int t, acc_t (&s)[NKB], acc_t (&sn)[NKB], const __bf16 *Kn, const __bf16 *Vs) {
+    auto step = [&](int t, acc_t (&s)[NKB], acc_t (&sn)[NKB], const T *Kn, const T *Vs) {
         const int kbase = t * BC;
         const bool edge = (kbase + BC > kv_len) || (CAUSAL && kbase + BC - 1 > wq0);
         if (edge) {
@@ -287,20 +291,20 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
         int kb0 = kbase0;
         asm volatile("" : "+v"(kb0));
 
-        bf16x8_t kf[NA], vf[NB], pf[NF];
+        x8_t kf[NA], vf[NB], pf[NF];
         float mx = kNegInf, alpha = 1.f, neg_m = 0.f, rs = 0.f;
         bool rescale = true;
 
         auto kread = [&](auto A) {
             constexpr int a = decltype(A)::value, ks = a / NKB, kb = a % NKB;
-            kf[a] = *reinterpret_cast<const bf16x8_t *>(Kn + kb * 32 * D + (kb0 ^ (ks << 4)));
+            kf[a] = *reinterpret_cast<const x8_t *>(Kn + kb * 32 * D + (kb0 ^ (ks << 4)));
         };
         auto vread = [&](auto PV) {
             constexpr int pv = decltype(PV)::value, f = pv / ND, mb = pv % ND;
-            const __bf16 *vp = Vs + ((f / 2) * 32 + (f % 2) * 16) * D + vaddr[mb];
+            const T *vp = Vs + ((f / 2) * 32 + (f % 2) * 16) * D + vaddr[mb];
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)vp);
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vp + 8 * D));
-            vf[pv] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            vf[pv] = __builtin_bit_cast(x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         // Fragment f holds scores s[f/2][8*(f%2) .. 8*(f%2)+7] of each lane.
         auto chunk = [&](auto K) {
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
                 for (int j = 0; j < 4; ++j) s[kb][j0 + j] = e[j];
             } else if constexpr (kind == kChunkCvt) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) pf[f][j] = (__bf16)s[kb][i0 + j];
+                for (int j = 0; j < 8; ++j) pf[f][j] = (T)s[kb][i0 + j];
                 pin(pf[f]);
             } else {
 #pragma unroll
@@ -353,13 +357,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
                 constexpr int ks = g / NKB, kb = g % NKB;
                 if constexpr (ks == 0) {
                     const acc_t zero = {};
-                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g], qf[ks], zero, 0, 0, 0);
+                    sn[kb] = E::mfma(kf[g], qf[ks], zero);
                 } else {
-                    sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g], qf[ks], sn[kb], 0, 0, 0);
+                    sn[kb] = E::mfma(kf[g], qf[ks], sn[kb]);
                 }
             } else {
                 constexpr int pv = g - NA, f = pv / ND, mb = pv % ND;
-                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[pv], pf[f], o[mb], 0, 0, 0);
+                o[mb] = E::mfma(vf[pv], pf[f], o[mb]);
             }
             static_for<Plan::NCH>([&](auto K) {
                 if constexpr (Plan::slot(decltype(K)::value, NS) == g) chunk(K);
@@ -446,15 +450,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
         const float l_tot = group_sum<32>(l);
         if (qrow < N) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            __bf16 *orow = O + (int64_t)qrow * D;
+            T *orow = O + (int64_t)qrow * D;
 #pragma unroll
             for (int mb = 0; mb < ND; ++mb)
 #pragma unroll
                 for (int gg = 0; gg < 4; ++gg) {
-                    bf16x4_t w;
+                    x4_t w;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) w[j] = (__bf16)(o[mb][4 * gg + j] * inv);
-                    *reinterpret_cast<bf16x4_t *>(orow + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
+                    for (int j = 0; j < 4; ++j) w[j] = (T)(o[mb][4 * gg + j] * inv);
+                    *reinterpret_cast<x4_t *>(orow + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
                 }
             if (a.lse && lane < 32)
                 a.lse[(int64_t)bh * N + qrow] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
@@ -462,27 +466,36 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_bf16_pipe(FwdArg
     }
 }
 
-template <int D, int BC, int NSTAGE, int NW, bool CAUSAL>
+template <class T, int D, int BC, int NSTAGE, int NW, bool CAUSAL>
 hipError_t launch_pipe(const FwdArgs &a, hipStream_t stream) {
     constexpr int BR = 32 * NW;
     const int nqt = (a.N + BR - 1) / BR;
-    hipLaunchKernelGGL((fwd_bf16_pipe<D, BC, NSTAGE, NW, CAUSAL>),
+    hipLaunchKernelGGL((fwd_pipe<T, D, BC, NSTAGE, NW, CAUSAL>),
                        dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-#define FA_PIPE(D, BC, NS, NW) \
-    Instance{D, 0, 32 * NW, BC, &launch_pipe<D, BC, NS, NW, false>}, \
-    Instance{D, 1, 32 * NW, BC, &launch_pipe<D, BC, NS, NW, true>}
+#define FA_PIPE(T, D, BC, NS, NW) \
+    Instance{D, 0, 32 * NW, BC, &launch_pipe<T, D, BC, NS, NW, false>}, \
+    Instance{D, 1, 32 * NW, BC, &launch_pipe<T, D, BC, NS, NW, true>}
 
 }  // namespace
 
 const Instance *bf16_tuned_instances() {
     static const Instance table[] = {
-        FA_PIPE(64, 64, 2, 4),
-        FA_PIPE(64, 64, 2, 8),
-        FA_PIPE(128, 64, 2, 4),
-        FA_PIPE(128, 64, 2, 8),
+        FA_PIPE(__bf16, 64, 64, 2, 4),
+        FA_PIPE(__bf16, 64, 64, 2, 8),
+        FA_PIPE(__bf16, 128, 64, 2, 4),
+        FA_PIPE(__bf16, 128, 64, 2, 8),
+        Instance{0, 0, 0, 0, nullptr},
+    };
+    return table;
+}
+
+const Instance *f16_tuned_instances() {
+    static const Instance table[] = {
+        FA_PIPE(_Float16, 64, 64, 2, 4),
+        FA_PIPE(_Float16, 128, 64, 2, 4),
         Instance{0, 0, 0, 0, nullptr},
     };
     return table;

@@ -40,6 +40,7 @@ struct Instance {
 // tile-size-study kernels and the fp32 kernels; and the default tile per head
 // size.  Tuned bf16 tiles with Br > 128 do not take a block mask.
 const Instance *bf16_tuned_instances();
+const Instance *f16_tuned_instances();
 const Instance *bf16_instances();
 const Instance *f32_instances();
 void bf16_default_tile(int d, int block_sparse, int *br, int *bc);

@@ -58,7 +58,8 @@ def call(**kw):
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(B=1 << 20, H=1 << 10, N=1 << 10), 2),
     (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
     (dict(q=Q + 8), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4), (dict(key_len=0x60000002), 4),
-    (dict(Br=48, Bc=64), 5), (dict(Br=128, Bc=256), 5), (dict(dtype=2), 5),
+    (dict(Br=48, Bc=64), 5), (dict(Br=128, Bc=256), 5), (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(dtype=2, Br=64, Bc=32), 5),
     (dict(dtype=1, Br=16, Bc=16), 5), (dict(d=64, Br=16, Bc=16), 5),
     (dict(Br=256, Bc=64, block_mask=0x70000000), 5),
     (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
@@ -122,6 +123,10 @@ def test_tile_table():
     assert fa.fa_tile_shape(fa.DTYPE_BF16, 64, False, 128, 64) == (128, 64)
     assert fa.fa_tile_shape(fa.DTYPE_BF16, 128, False, 256, 64) == (256, 64)
     assert fa.fa_tile_shape(fa.DTYPE_F32, 64) == (128, 32)
+    for d in (64, 128):
+        assert fa.fa_tile_shape(fa.DTYPE_F16, d) == (128, 64)
+    with pytest.raises(fa.FaError):
+        fa.fa_tile_shape(fa.DTYPE_F16, 128, False, 64, 32)
     with pytest.raises(fa.FaError):
         fa.fa_tile_shape(fa.DTYPE_BF16, 128, True, 256, 64)
     with pytest.raises(fa.FaError):

@@ -17,13 +17,28 @@ torch = pytest.importorskip("torch")
 
 import io_aware_exact_03_amd as fa  # noqa: E402
 import oracle  # noqa: E402
-from workloads import WORKLOADS, make_inputs, random_qkv, band_global_block_mask  # noqa: E402
+from workloads import WORKLOADS, make_inputs, random_qkv, band_global_block_mask, causal_prefix  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-5
 TOL_BF16 = 2e-2
 TOL_LSE = 1e-3
+# fp16 I/O: O is rounded to fp16 once (half an ulp is <= 2^-11 for |O| < 2,
+# <= 2^-10 below 4) and each probability once (relative 2^-11, which moves O
+# by at most 2^-11 * max|v| ~ 2.4e-3 for |v| <= 5, far less for random
+# signs); 4e-3 covers both with margin.
+TOL_F16 = 4e-3
+
+
+_PREFIX = {}
+
+
+def long_causal_prefix():
+    """Rows 0..2047 of heads 0..3 of the 16K causal workload (drawn once)."""
+    if "x" not in _PREFIX:
+        _PREFIX["x"] = causal_prefix(WORKLOADS["long_causal"], N=2048, H=4)
+    return dict(_PREFIX["x"])
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -34,7 +49,8 @@ def _need_gpu():
 
 def to_dev(x, dtype):
     t = torch.from_numpy(np.ascontiguousarray(x))
-    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(dtype, torch.float32)
+    return t.to(tdt).cuda()
 
 
 def run(inp, dtype="bf16", Br=0, Bc=0, scale=None, causal=None):
@@ -163,10 +179,11 @@ def test_large_workloads_sampled_rows(name):
 def test_tile_sweep_slice(Br, Bc):
     """The 16 (Br, Bc) tiles on the first 2048 rows of heads 0-3 of the 16K
     causal workload (a self-contained causal prefix)."""
-    w = WORKLOADS["long_causal"]
-    inp = make_inputs(w, N=2048, H=4)
+    inp = long_causal_prefix()
+    if "ref" not in _PREFIX:
+        _PREFIX["ref"] = ref(inp)
     o, lse = run(inp, Br=Br, Bc=Bc)
-    check(o, lse, *ref(inp), TOL_BF16, f"sweep Br={Br} Bc={Bc}")
+    check(o, lse, *_PREFIX["ref"], TOL_BF16, f"sweep Br={Br} Bc={Bc}")
 
 
 # ---------------------------------------------------------------- closed forms on the GPU
@@ -333,3 +350,28 @@ def test_gqa_matches_repeated_key_values_bitwise():
     o2, lse2 = run(rep)
     np.testing.assert_array_equal(o, o2)
     np.testing.assert_array_equal(lse, lse2)
+
+
+# ---------------------------------------------------------------- fp16 I/O
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 129, 300])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_f16_modes(d, N, mode):
+    inp = custom(2, 2, N, d, seed=50 + N + d, dtype="f16", **modes_for(N, 51)[mode])
+    o, lse = run(inp, "f16")
+    check(o, lse, *ref(inp), TOL_F16, f"f16 d={d} N={N} {mode}")
+
+
+def test_f16_gqa_and_negative_scale():
+    inp = gqa_custom(1, 4, 2, 200, 128, seed=52, dtype="f16", causal=True)
+    o, lse = run(inp, "f16", scale=-0.1)
+    check(o, lse, *ref(inp, scale=-0.1), TOL_F16, "f16 gqa scale=-0.1")
+
+
+def test_f16_long_causal_slice():
+    """The 16K causal workload's B1 H4 N2048 prefix, rounded to fp16."""
+    inp = causal_prefix(WORKLOADS["long_causal"], N=2048, H=4, fmt="f16")
+    o, lse = run(inp, "f16")
+    check(o, lse, *ref(inp), TOL_F16, "f16 long_causal slice")

@@ -89,8 +89,14 @@ def band_global_block_mask(nb, rng, n_global=4, radius=1):
     return m.reshape(-1)
 
 
+def f16_round(x):
+    """float32 array -> float32 array of the nearest IEEE half values (RNE)."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 def random_qkv(B, H, N, d, seed, dtype="bf16", amp=1.0, rng=None):
-    """Q, K, V as float32 [B,H,N,d] (bf16-representable when dtype='bf16')."""
+    """Q, K, V as float32 [B,H,N,d] (bf16- or fp16-representable when dtype is
+    'bf16' or 'f16'; the unrounded float32 draw otherwise)."""
     if rng is None:
         rng = np.random.Generator(np.random.PCG64(seed))
     out = []
@@ -100,8 +106,27 @@ def random_qkv(B, H, N, d, seed, dtype="bf16", amp=1.0, rng=None):
             x *= np.float32(amp)
         if dtype == "bf16":
             x = bf16_round(x)
+        elif dtype == "f16":
+            x = f16_round(x)
         out.append(x)
     return out[0], out[1], out[2], rng
+
+
+def causal_prefix(w, N, H, fmt=None):
+    """Rows 0..N-1 of heads 0..H-1 of causal workload ``w``'s full tensors.
+
+    Under a causal mask these rows attend only to keys 0..N-1, so the slice
+    is a self-contained problem whose exact outputs are those rows of the
+    full problem.  ``fmt`` re-rounds the workload's float32 draw to another
+    I/O format instead ("f32": unrounded, "f16": IEEE half, "bf16").
+    Returns a dict like make_inputs.
+    """
+    if not w.causal or w.key_len_range is not None or w.sparse_globals:
+        raise ValueError("causal_prefix needs a plain causal workload")
+    q, k, v, _ = random_qkv(w.B, w.H, w.N, w.d, w.seed, fmt or w.dtype, w.amp)
+    cut = lambda x: np.ascontiguousarray(x[:, :H, :N])
+    return dict(q=cut(q), k=cut(k), v=cut(v), key_len=None, block_mask=None,
+                scale=w.scale, causal=True)
 
 
 def make_inputs(w, N=None, H=None, B=None):
