@@ -71,7 +71,8 @@ typedef enum {
     FA_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte, lse/key_len not 4-byte */
     FA_ERR_UNSUPPORTED_TILE = 5,     /* (Br, Bc) pair or dtype not built            */
     FA_ERR_HIP = 6,                  /* the kernel launch failed                    */
-    FA_ERR_INVALID_ARG = 7           /* non-finite scale, o overlapping an input    */
+    FA_ERR_INVALID_ARG = 7           /* non-finite scale, o overlapping an input,
+                                        unknown tile order                          */
 } fa_status;
 
 /* Element type codes for fa_fwd_ex and fa_fwd_gqa.  FA_DTYPE_F16 (IEEE
@@ -121,6 +122,27 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N, int d, float scale, int causal,
               const int32_t *key_len, const uint8_t *block_mask,
               hipStream_t stream, int dtype, int Br, int Bc);
+
+/* Key-tile visit orders for fa_fwd_study. */
+enum { FA_ORDER_ASCENDING = 0, FA_ORDER_DESCENDING = 1 };
+
+/*
+ * Tile-order control for the deviation study: the page "Is Flash Attention
+ * Stable?" explainer (aibr.jp, sections 2 and 3) varies the order in which
+ * blocks/tiles are processed besides their sizes, and asks libraries to
+ * expose such settings (section 6).  Same arguments as fa_fwd_ex plus
+ *   tile_order : FA_ORDER_ASCENDING (key tiles 0, 1, ...; what every other
+ *                entry point does) or FA_ORDER_DESCENDING (last key tile
+ *                first).  Other values: FA_ERR_INVALID_ARG.
+ * The result is the same attention up to rounding; only the order of the
+ * running-maximum/rescale steps changes.  FA_ORDER_DESCENDING runs on the
+ * tile-study kernels only (bf16, d = 128, explicit Br, Bc in
+ * {16, 32, 64, 128}); other tiles return FA_ERR_UNSUPPORTED_TILE.
+ */
+int fa_fwd_study(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const int32_t *key_len, const uint8_t *block_mask,
+                 hipStream_t stream, int dtype, int Br, int Bc, int tile_order);
 
 /*
  * Grouped-query attention: the H query heads of each batch entry are split

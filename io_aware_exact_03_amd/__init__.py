@@ -1,7 +1,7 @@
 """Python binding of the gfx950 exact-attention forward library (libfa.so).
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
-``fa_fwd_ex``, ``fa_fwd_gqa``, ``fa_tile_shape``, ``fa_status_string``,
+``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_tile_shape``, ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
 the library's HIP kernels.  ``fwd`` is a convenience wrapper that allocates
@@ -12,7 +12,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_gqa", "fa_tile_shape",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa",
+           "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
            "DTYPE_BF16", "DTYPE_F32", "DTYPE_F16", "MASK_BLOCK"]
 
@@ -20,6 +21,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 DTYPE_F16 = 2
+ORDER_ASCENDING = 0
+ORDER_DESCENDING = 1
 MASK_BLOCK = 128
 
 FA_OK = 0
@@ -60,6 +63,8 @@ def _load():
     lib.fa_fwd_f32.restype = i32
     lib.fa_fwd_ex.argtypes = fwd_args + [i32, i32, i32]
     lib.fa_fwd_ex.restype = i32
+    lib.fa_fwd_study.argtypes = fwd_args + [i32, i32, i32, i32]
+    lib.fa_fwd_study.restype = i32
     lib.fa_fwd_gqa.argtypes = fwd_args[:7] + [i32] + fwd_args[7:] + [i32, i32, i32]
     lib.fa_fwd_gqa.restype = i32
     lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -98,6 +103,13 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, s
                              key_len, block_mask, stream, dtype, Br, Bc), "fa_fwd_ex")
 
 
+def fa_fwd_study(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream,
+                 dtype, Br, Bc, tile_order):
+    _check(_load().fa_fwd_study(q, k, v, o, lse, B, H, N, d, scale, int(bool(causal)),
+                                key_len, block_mask, stream, dtype, Br, Bc, tile_order),
+           "fa_fwd_study")
+
+
 def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
                dtype, Br, Bc):
     _check(_load().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, int(bool(causal)),
@@ -123,7 +135,7 @@ def fa_last_hip_error():
 
 
 def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, Bc=0,
-        out=None, lse=None, stream=None):
+        out=None, lse=None, stream=None, tile_order=ORDER_ASCENDING):
     """Attention forward on device tensors.
 
     q: contiguous [B, H, N, d] cuda tensor, bfloat16, float16 or float32; k, v: the
@@ -133,7 +145,8 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
     ceil(N/128)^2 entries (row = query block) or None.  scale defaults to
     1/sqrt(d).  Br/Bc = 0 selects the tuned tile.  Returns (o, lse) with o like
     q and lse float32 [B, H, N]; `out`/`lse` may be passed preallocated, and
-    lse=False skips the logsumexp (returned as None).
+    lse=False skips the logsumexp (returned as None).  tile_order =
+    ORDER_DESCENDING visits key tiles last-first (tile-study kernels only).
     """
     import torch
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -173,7 +186,13 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
         bm_ptr = block_mask.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    if H_kv == H:
+    if tile_order != ORDER_ASCENDING:
+        if H_kv != H:
+            raise ValueError("tile_order applies to plain multi-head calls only")
+        fa_fwd_study(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                     lse.data_ptr() if want_lse else None, B, H, N, d, float(scale),
+                     causal, kl_ptr, bm_ptr, stream, dtype, Br, Bc, tile_order)
+    elif H_kv == H:
         fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                   lse.data_ptr() if want_lse else None, B, H, N, d, float(scale),
                   causal, kl_ptr, bm_ptr, stream, dtype, Br, Bc)

@@ -32,7 +32,8 @@ const fa::Instance *find(const fa::Instance *table, int d, int causal, int br, i
 // there is one, else a tuned kernel of that shape.  Tuned tiles taller than
 // one 128-token mask block do not take a block mask.
 int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
-                 const fa::Instance **out, int *br_out, int *bc_out) {
+                 const fa::Instance **out, int *br_out, int *bc_out, bool *study = nullptr) {
+    if (study) *study = false;
     if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16)
         return FA_ERR_UNSUPPORTED_TILE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -48,6 +49,7 @@ int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
         inst = find(fa::bf16_tuned_instances(), d, causal, br, bc);
     } else {
         inst = find(fa::bf16_instances(), d, causal, br, bc);
+        if (inst && study) *study = true;
         if (!inst && (!block_sparse || br <= 128)) inst = find(fa::bf16_tuned_instances(), d, causal, br, bc);
     }
     if (!inst) return FA_ERR_UNSUPPORTED_TILE;
@@ -59,7 +61,8 @@ int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
 
 int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
             int Hkv, int N, int d, float scale, int causal, const int32_t *key_len,
-            const uint8_t *block_mask, hipStream_t stream, int dtype, int br, int bc) {
+            const uint8_t *block_mask, hipStream_t stream, int dtype, int br, int bc,
+            int order = FA_ORDER_ASCENDING) {
     if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
     if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -80,10 +83,14 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     const uint64_t lse_bytes = (uint64_t)B * H * N * sizeof(float);
     if (lse && overlaps(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
 
+    if (order != FA_ORDER_ASCENDING && order != FA_ORDER_DESCENDING) return FA_ERR_INVALID_ARG;
     int tbr = 0, tbc = 0;
     const fa::Instance *inst = nullptr;
-    const int rc = resolve_tile(dtype, d, block_mask != nullptr, br, bc, causal ? 1 : 0, &inst, &tbr, &tbc);
+    bool study = false;
+    const int rc = resolve_tile(dtype, d, block_mask != nullptr, br, bc, causal ? 1 : 0, &inst, &tbr,
+                                &tbc, &study);
     if (rc != FA_OK) return rc;
+    if (order != FA_ORDER_ASCENDING && !study) return FA_ERR_UNSUPPORTED_TILE;
 
     fa::FwdArgs a;
     a.q = q;
@@ -99,6 +106,7 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     a.Hkv = Hkv;
     a.group = H / Hkv;
     a.nkb = (N + 127) / 128;
+    a.order = order;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
     const hipError_t err = inst->launch(a, stream);
@@ -134,6 +142,14 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse, 
                    Br, Bc);
 }
 
+int fa_fwd_study(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                 int N, int d, float scale, int causal, const int32_t *key_len,
+                 const uint8_t *block_mask, hipStream_t stream, int dtype, int Br, int Bc,
+                 int tile_order) {
+    return forward(q, k, v, o, lse, B, H, H, N, d, scale, causal, key_len, block_mask, stream,
+                   dtype, Br, Bc, tile_order);
+}
+
 int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                int H_kv, int N, int d, float scale, int causal, const int32_t *key_len,
                const uint8_t *block_mask, hipStream_t stream, int dtype, int Br, int Bc) {
@@ -156,7 +172,8 @@ const char *fa_status_string(int status) {
         case FA_ERR_MISALIGNED: return "misaligned pointer (q/k/v/o need 16 bytes, lse/key_len 4)";
         case FA_ERR_UNSUPPORTED_TILE: return "unsupported dtype or tile shape";
         case FA_ERR_HIP: return "HIP launch error (see fa_last_hip_error)";
-        case FA_ERR_INVALID_ARG: return "invalid argument (non-finite scale or overlapping output)";
+        case FA_ERR_INVALID_ARG:
+            return "invalid argument (non-finite scale, overlapping output or unknown tile order)";
         default: return "unknown status";
     }
 }

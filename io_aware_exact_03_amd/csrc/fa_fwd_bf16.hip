@@ -110,6 +110,36 @@ __global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf
         if (blk == blk0) return t;
         return blk >= a.nkb ? ntiles : min(ntiles, blk * (128 / BC));
     };
+    // Largest active tile <= t (-1 if none): the same scan downwards.
+    auto prev_tile = [&](int t) {
+        if (!mrow || t < 0) return t;
+        int blk = (t * BC) >> 7;
+        const int blk0 = blk;
+        while (blk >= 0) {
+            const int ch = blk >> 6;
+            if (ch != mask_chunk) {
+                const int idx = ch * 64 + lane;
+                mask_bits = __builtin_amdgcn_ballot_w64(idx < a.nkb && mrow[idx] != 0);
+                mask_chunk = ch;
+            }
+            const int bit = blk & 63;
+            const uint64_t below = bit == 63 ? ~0ull : ((1ull << (bit + 1)) - 1);
+            const uint64_t rest = mask_bits & below;
+            if (rest) {
+                blk = ch * 64 + 63 - __builtin_clzll(rest);
+                break;
+            }
+            blk = ch * 64 - 1;
+        }
+        if (blk == blk0) return t;
+        return blk < 0 ? -1 : min(ntiles - 1, blk * (128 / BC) + 128 / BC - 1);
+    };
+    // Key tiles are visited in ascending order, or descending when asked
+    // (the tile-order axis of the deviation study).
+    const bool descending = a.order == 1;
+    auto first_tile = [&]() { return descending ? prev_tile(ntiles - 1) : next_tile(0); };
+    auto following = [&](int t) { return descending ? prev_tile(t - 1) : next_tile(t + 1); };
+    auto valid = [&](int t) { return t >= 0 && t < ntiles; };
 
     // Q fragments (B operand of S^T = K Q^T), resident for the whole kernel.
     // A negative scale is folded into Q (sign flip, exact) so that c >= 0.
@@ -246,20 +276,20 @@ __global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf
     // LDS buffers: wait for tile t, barrier (all waves are also done with the
     // other buffer), start copying the next tile into the other buffer,
     // compute tile t.
-    int t = next_tile(0);
-    if (t < ntiles) copy_tile<C, D>(K, V, k_lds0, v_lds0, t * BC, klast, wave, lane);
-    while (t < ntiles) {
-        int tn = next_tile(t + 1);
+    int t = first_tile();
+    if (valid(t)) copy_tile<C, D>(K, V, k_lds0, v_lds0, t * BC, klast, wave, lane);
+    while (valid(t)) {
+        int tn = following(t);
         wait_copies();
         __syncthreads();
-        if (tn < ntiles) copy_tile<C, D>(K, V, k_lds1, v_lds1, tn * BC, klast, wave, lane);
+        if (valid(tn)) copy_tile<C, D>(K, V, k_lds1, v_lds1, tn * BC, klast, wave, lane);
         compute(t, k_lds0, v_lds0);
         t = tn;
-        if (t >= ntiles) break;
-        tn = next_tile(t + 1);
+        if (!valid(t)) break;
+        tn = following(t);
         wait_copies();
         __syncthreads();
-        if (tn < ntiles) copy_tile<C, D>(K, V, k_lds0, v_lds0, tn * BC, klast, wave, lane);
+        if (valid(tn)) copy_tile<C, D>(K, V, k_lds0, v_lds0, tn * BC, klast, wave, lane);
         compute(t, k_lds1, v_lds1);
         t = tn;
     }

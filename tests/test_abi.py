@@ -25,8 +25,8 @@ def declared_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_gqa",
-                                           "fa_tile_shape", "fa_status_string",
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study",
+                                           "fa_fwd_gqa", "fa_tile_shape", "fa_status_string",
                                            "fa_last_hip_error"])
 
 
@@ -89,6 +89,25 @@ def call_gqa(**kw):
 ])
 def test_gqa_invalid_arguments_return_status_without_launch(kw, status):
     assert call_gqa(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(order=2), 7), (dict(order=-1), 7),
+    # descending order only on the tile-study kernels (bf16, d = 128, explicit tile)
+    (dict(order=1), 5), (dict(order=1, d=64, Br=128, Bc=64), 5),
+    (dict(order=1, dtype=1), 5), (dict(order=1, Br=256, Bc=64), 5), (dict(order=1, dtype=2, Br=128, Bc=64), 5),
+    (dict(order=1, d=128, Br=64, Bc=32, q=None), 1),
+])
+def test_study_order_validation(kw, status):
+    args = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, N=100, d=128, scale=0.125, causal=0,
+                key_len=None, block_mask=None, stream=None, dtype=0, Br=0, Bc=0, order=0)
+    args.update(kw)
+    lib = fa._load()
+    rc = lib.fa_fwd_study(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                          args["H"], args["N"], args["d"], args["scale"], args["causal"],
+                          args["key_len"], args["block_mask"], args["stream"], args["dtype"],
+                          args["Br"], args["Bc"], args["order"])
+    assert rc == status
 
 
 def test_status_strings_cover_every_code():

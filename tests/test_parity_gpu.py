@@ -375,3 +375,32 @@ def test_f16_long_causal_slice():
     inp = causal_prefix(WORKLOADS["long_causal"], N=2048, H=4, fmt="f16")
     o, lse = run(inp, "f16")
     check(o, lse, *ref(inp), TOL_F16, "f16 long_causal slice")
+
+
+# ---------------------------------------------------------------- tile order (deviation study)
+
+
+@pytest.mark.parametrize("Br,Bc", [(16, 16), (64, 32), (128, 128)])
+@pytest.mark.parametrize("N", [300, 1000])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_descending_tile_order(Br, Bc, N, mode):
+    inp = custom(2, 2, N, 128, seed=60 + N + Br, **modes_for(N, 61)[mode])
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    kl = torch.from_numpy(inp["key_len"]).cuda() if inp.get("key_len") is not None else None
+    bm = torch.from_numpy(inp["block_mask"]).cuda() if inp.get("block_mask") is not None else None
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd(q, k, v, causal=inp["causal"], key_len=kl, block_mask=bm, scale=float(inp["scale"]),
+           Br=Br, Bc=Bc, out=out, lse=lse, tile_order=fa.ORDER_DESCENDING)
+    torch.cuda.synchronize()
+    check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16,
+          f"descending Br={Br} Bc={Bc} N={N} {mode}")
+
+
+def test_descending_tile_order_fully_masked_rows():
+    inp = custom(2, 2, 200, 128, seed=62, key_len=[0, 130])
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    kl = torch.from_numpy(inp["key_len"]).cuda()
+    out, lse = fa.fwd(q, k, v, key_len=kl, Br=32, Bc=64, tile_order=fa.ORDER_DESCENDING)
+    torch.cuda.synchronize()
+    check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16, "desc masked")

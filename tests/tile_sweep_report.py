@@ -9,7 +9,8 @@ The slice is rows 0..2047 of heads 0..3 of the 16K causal workload's tensors
 self-contained problem.  The precision rows feed the same float32 draw
 rounded to fp16, or unrounded to the fp32 path.
 
-For every (Br, Bc) it prints max|dO|, mean|dO|, max|dLSE| against the oracle
+It also runs a few tiles with the key tiles visited last-first (the
+tile-order axis of the same study).  For every (Br, Bc) it prints max|dO|, mean|dO|, max|dLSE| against the oracle
 and the kernel time per launch (HIP events on the launch stream).  The trend
 is reported, not asserted; the per-point bar (max|dO| <= 2e-2) is asserted by
 the GPU parity tests.
@@ -32,6 +33,8 @@ import oracle  # noqa: E402
 from workloads import WORKLOADS, causal_prefix  # noqa: E402
 
 PAIRS = [(br, bc) for br in (16, 32, 64, 128) for bc in (16, 32, 64, 128)] + [(256, 64), (0, 0)]
+# the tile-order axis: descending key-tile order on the tile-study kernels
+DESC = [(16, 16), (32, 64), (64, 64), (128, 16), (128, 64), (128, 128)]
 
 
 def main():
@@ -48,9 +51,10 @@ def main():
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     pairs = 4 * 2048 * 2049 // 2
     rows = []
-    for br, bc in PAIRS:
+    for br, bc, order in [(br, bc, 0) for br, bc in PAIRS] + [(br, bc, 1) for br, bc in DESC]:
         def call():
-            fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, out=out, lse=lse)
+            fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, out=out, lse=lse,
+                   tile_order=order)
         call()
         torch.cuda.synchronize()
         o = out.double().cpu().numpy()
@@ -68,7 +72,8 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.reps
         tb, tc = fa.fa_tile_shape(0, 128, False, br, bc)
-        rows.append(dict(Br=tb, Bc=tc, default=(br, bc) == (0, 0), max_dO=float(d_o.max()),
+        rows.append(dict(Br=tb, Bc=tc, default=(br, bc) == (0, 0), order="desc" if order else "asc",
+                         max_dO=float(d_o.max()),
                          mean_dO=float(d_o.mean()), max_dLSE=float(d_l.max()), us=us,
                          tflops=4 * 128 * pairs / (us * 1e-6) / 1e12))
     # Precision axis: the same float32 draw rounded to each I/O format, each
@@ -83,14 +88,14 @@ def main():
         d_o = np.abs(oo.double().cpu().numpy() - o_r)
         d_l = np.abs(lse.double().cpu().numpy() - l_r)
         tb, tc = fa.fa_tile_shape(fa.DTYPE_F16 if fmt == "f16" else fa.DTYPE_F32, 128)
-        rows.append(dict(Br=tb, Bc=tc, default=True, fmt=fmt, max_dO=float(d_o.max()),
+        rows.append(dict(Br=tb, Bc=tc, default=True, fmt=fmt, order="asc", max_dO=float(d_o.max()),
                          mean_dO=float(d_o.mean()), max_dLSE=float(d_l.max()), us=float("nan"),
                          tflops=float("nan")))
-    print("| I/O | Br | Bc | max abs dO | mean abs dO | max abs dLSE | us/launch | TFLOP/s |")
-    print("|---|---|---|---|---|---|---|---|")
+    print("| I/O | order | Br | Bc | max abs dO | mean abs dO | max abs dLSE | us/launch | TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         tag = " (default)" if r["default"] else ""
-        print(f"| {r.get('fmt', 'bf16')} | {r['Br']}{tag} | {r['Bc']} | {r['max_dO']:.3e} | {r['mean_dO']:.3e} | "
+        print(f"| {r.get('fmt', 'bf16')} | {r['order']} | {r['Br']}{tag} | {r['Bc']} | {r['max_dO']:.3e} | {r['mean_dO']:.3e} | "
               f"{r['max_dLSE']:.3e} | {r['us']:.1f} | {r['tflops']:.1f} |", flush=True)
     if args.json:
         with open(args.json, "w") as f:
