@@ -12,6 +12,8 @@ A = row-softmax(S), O = A V, plus the row logsumexp (natural log).
 The C implementation (attn_ref.c) materialises S one head at a time;
 ``attention_rows_f64`` does the same for a list of query rows only, for
 sampled checks at sizes where a full pass would take too long.
+``attention_bwd_f64`` gives the gradients of that definition (dQ, dK, dV for
+a given dO), derived from it by the chain rule.
 
 Inputs are widened exactly to float64 (float32 and bfloat16 values are
 representable), so the oracle sees precisely the values the GPU receives.
@@ -47,6 +49,10 @@ def _configure(lib):
                                           ctypes.c_void_p, ctypes.c_void_p, i64,
                                           ctypes.c_void_p, i64, dp, dp]
     lib.attn_ref_rows_gqa_f64.restype = ctypes.c_int
+    lib.attn_bwd_ref_gqa_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                         ctypes.c_double, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p, i64]
+    lib.attn_bwd_ref_gqa_f64.restype = ctypes.c_int
     lib.attn_ref_threads.restype = ctypes.c_int
     return lib
 
@@ -135,9 +141,31 @@ def attention_rows_f64(q, k, v, rows, scale, causal=False, key_len=None,
     return o, lse
 
 
+def attention_bwd_f64(q, k, v, dout, scale, causal=False, key_len=None, block_mask=None,
+                      block=128):
+    """Gradients (dQ, dK, dV) in float64 of the loss sum(dout * O) for the
+    attention definition above; k, v (and dK, dV) may have H_kv < H heads."""
+    q, k, v, kl, bm = _prep(q, k, v, key_len, block_mask, block)
+    dout = _f64(dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    B, H, N, d = q.shape
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _load().attn_bwd_ref_gqa_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, k.shape[1], N, d, float(scale), int(bool(causal)),
+        kl.ctypes.data if kl is not None else None,
+        bm.ctypes.data if bm is not None else None, block)
+    if rc != 0:
+        raise RuntimeError(f"attn_bwd_ref_gqa_f64 failed with code {rc}")
+    return dq, dk, dv
+
+
 def threads():
     """OpenMP threads the oracle's parallel regions use."""
     return int(_load().attn_ref_threads())
 
 
-__all__ = ["attention_f64", "attention_rows_f64", "threads"]
+__all__ = ["attention_f64", "attention_rows_f64", "attention_bwd_f64", "threads"]

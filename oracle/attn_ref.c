@@ -213,6 +213,103 @@ int attn_ref_rows_f64(const double *q, const double *k, const double *v,
                                  block_mask, blk, rows, n_rows, o_rows, lse_rows);
 }
 
+/* Gradients of the definition (backward pass) -- not printed on the pages,
+ * which give only the forward definition; this is its derivative, written
+ * out plainly.  With the loss L = sum_{i,c} dO_ic O_ic (so dL/dO = dO):
+ *     A_ij  = softmax_j(S_ij)               (0 for disallowed keys)
+ *     dV_j  = sum_i A_ij dO_i
+ *     dA_ij = dO_i . V_j
+ *     D_i   = dO_i . O_i  (= sum_j A_ij dA_ij)
+ *     dS_ij = A_ij (dA_ij - D_i)
+ *     dQ_i  = scale * sum_j dS_ij K_j
+ *     dK_j  = scale * sum_i dS_ij Q_i
+ * With grouped key/value heads, dK and dV of a key/value head sum the
+ * contributions of every query head of its group.  One head at a time, A
+ * (then dS, in place) materialised as an N x N array of doubles.  dq is
+ * [B, H, N, d]; dk and dv are [B, Hkv, N, d] and are overwritten. */
+int attn_bwd_ref_gqa_f64(const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk, double *dv,
+                         int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                         double scale, int causal, const int32_t *key_len,
+                         const uint8_t *block_mask, int64_t blk)
+{
+    int rc = check_args(q, k, v, B, H, Hkv, N, d, block_mask, blk);
+    if (rc) return rc;
+    if (!dout || !dq || !dk || !dv) return 1;
+    for (int64_t x = 0; x < B * H * N * d; ++x) dq[x] = 0.0;
+    for (int64_t x = 0; x < B * Hkv * N * d; ++x) dk[x] = dv[x] = 0.0;
+    if (N == 0) return 0;
+    const int64_t nkb = block_mask ? (N + blk - 1) / blk : 0;
+    double *A = (double *)malloc((size_t)N * (size_t)N * sizeof(double));
+    double *O = (double *)malloc((size_t)N * (size_t)d * sizeof(double));
+    double *Dr = (double *)malloc((size_t)N * sizeof(double));
+    if (!A || !O || !Dr) {
+        free(A);
+        free(O);
+        free(Dr);
+        return 3;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t head = (b * H + h) * N, kvh = kv_head(b, h, H, Hkv) * N;
+            const double *qh = q + head * d, *kh = k + kvh * d, *vh = v + kvh * d;
+            const double *doh = dout + head * d;
+            double *dqh = dq + head * d, *dkh = dk + kvh * d, *dvh = dv + kvh * d;
+            /* A and O (the forward definition), D_i = dO_i . O_i */
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t i = 0; i < N; ++i) {
+                double lse_unused;
+                score_row(A + i * N, qh + i * d, kh, i, b, N, d, scale, causal,
+                          key_len, block_mask, blk, nkb);
+                softmax_row_times_v(A + i * N, vh, O + i * d, &lse_unused, N, d);
+                double acc = 0.0;
+                for (int64_t c = 0; c < d; ++c) acc += doh[i * d + c] * O[i * d + c];
+                Dr[i] = acc;
+            }
+            /* dV_j += sum_i A_ij dO_i */
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t j = 0; j < N; ++j) {
+                for (int64_t i = 0; i < N; ++i) {
+                    const double a = A[i * N + j];
+                    if (a == 0.0) continue;
+                    for (int64_t c = 0; c < d; ++c) dvh[j * d + c] += a * doh[i * d + c];
+                }
+            }
+            /* dS_ij = A_ij (dO_i . V_j - D_i), in place of A */
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t i = 0; i < N; ++i) {
+                for (int64_t j = 0; j < N; ++j) {
+                    const double a = A[i * N + j];
+                    if (a == 0.0) continue;
+                    double da = 0.0;
+                    for (int64_t c = 0; c < d; ++c) da += doh[i * d + c] * vh[j * d + c];
+                    A[i * N + j] = a * (da - Dr[i]);
+                }
+            }
+            /* dQ_i = scale sum_j dS_ij K_j */
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t i = 0; i < N; ++i)
+                for (int64_t j = 0; j < N; ++j) {
+                    const double ds = A[i * N + j];
+                    if (ds == 0.0) continue;
+                    for (int64_t c = 0; c < d; ++c) dqh[i * d + c] += scale * ds * kh[j * d + c];
+                }
+            /* dK_j += scale sum_i dS_ij Q_i */
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t j = 0; j < N; ++j)
+                for (int64_t i = 0; i < N; ++i) {
+                    const double ds = A[i * N + j];
+                    if (ds == 0.0) continue;
+                    for (int64_t c = 0; c < d; ++c) dkh[j * d + c] += scale * ds * qh[i * d + c];
+                }
+        }
+    }
+    free(A);
+    free(O);
+    free(Dr);
+    return 0;
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int attn_ref_threads(void)
 {

@@ -2,7 +2,8 @@
 
 Each case plants one mistake in a temporary copy of oracle/attn_ref.c (a
 dropped scale, an off-by-one mask, a transposed block mask, a dropped
-normalisation, a wrong operand, a sign error, ...), builds it with gcc, swaps
+normalisation, a wrong operand, a sign error, ..., and the same kinds of
+mistakes in the gradient code), builds it with gcc, swaps
 it in for the real oracle and runs a few fast pins from test_oracle.py.  At
 least one pin has to fail for every mutant.  CPU only.
 """
@@ -16,6 +17,7 @@ import pytest
 import oracle
 from oracle import build as obuild
 import test_oracle as pins
+import test_oracle_bwd as bwd_pins
 
 MUTANTS = {
     "dropped_scale": ("s[j] = scale * dot;", "s[j] = dot;"),
@@ -31,6 +33,14 @@ MUTANTS = {
     "dot_index": ("dot += qi[c] * kj[c];", "dot += qi[c] * kj[0];"),
     "value_index": ("o[c] += s[j] * vj[c];", "o[c] += s[j] * vj[0];"),
     "kv_heads_interleaved": ("return b * Hkv + h / (H / Hkv);", "return b * Hkv + h % Hkv;"),
+    # backward (gradient) mistakes
+    "bwd_no_delta": ("A[i * N + j] = a * (da - Dr[i]);", "A[i * N + j] = a * da;"),
+    "bwd_dk_unscaled": ("dkh[j * d + c] += scale * ds * qh[i * d + c];",
+                        "dkh[j * d + c] += ds * qh[i * d + c];"),
+    "bwd_dq_wrong_operand": ("dqh[i * d + c] += scale * ds * kh[j * d + c];",
+                             "dqh[i * d + c] += scale * ds * vh[j * d + c];"),
+    "bwd_dv_wrong_row": ("dvh[j * d + c] += a * doh[i * d + c];", "dvh[j * d + c] += a * doh[j * d + c];"),
+    "bwd_delta_sign": ("A[i * N + j] = a * (da - Dr[i]);", "A[i * N + j] = a * (da + Dr[i]);"),
 }
 
 FAST_PINS = [
@@ -40,6 +50,9 @@ FAST_PINS = [
     lambda: pins.test_identity_values_expose_attention_matrix("blocks"),
     lambda: pins.test_identity_values_expose_attention_matrix("padded"),
     pins.test_gqa_equals_multi_head_with_repeated_key_values,
+    lambda: bwd_pins.test_gradients_match_finite_differences(1, 1, "causal"),
+    lambda: bwd_pins.test_key_and_value_shift_invariances("dense"),
+    bwd_pins.test_grouped_heads_sum_the_group,
 ]
 
 
