@@ -162,6 +162,34 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
                const int32_t *key_len, const uint8_t *block_mask,
                hipStream_t stream, int dtype, int Br, int Bc);
 
+/*
+ * Backward pass: the gradients of the loss sum(dout * o) with respect to q,
+ * k and v, for bf16 attention computed by fa_fwd / fa_fwd_gqa with the same
+ * scale, causal flag, key_len and block_mask.  The pages give only the
+ * forward definition (mdooai.com, "Core formula") and report training
+ * speed-ups (ai-paper-library, Summary); the gradients are the chain rule on
+ * that definition:
+ *     P = exp(S - LSE), dV = P^T dO, dP = dO V^T, Delta_i = dO_i . O_i,
+ *     dS = P (dP - Delta), dQ = scale dS K, dK = scale dS^T Q,
+ * with P recomputed tile by tile from q, k and the forward's lse (never
+ * stored); dK and dV of a shared key/value head sum over its query heads.
+ *   q, o, dout : DEVICE bf16 [B, H, N, d]      k, v : bf16 [B, H_kv, N, d]
+ *   lse        : DEVICE float [B, H, N], the forward's logsumexp (natural log)
+ *   delta      : DEVICE float [B, H, N] workspace owned by the caller,
+ *                overwritten (holds Delta after the call)
+ *   dq         : DEVICE bf16 [B, H, N, d] output
+ *   dk, dv     : DEVICE bf16 [B, H_kv, N, d] outputs
+ * All 16-byte aligned (lse, delta, key_len: 4).  Outputs and workspace must
+ * not overlap the inputs or each other (FA_ERR_INVALID_ARG).  Same status
+ * codes and asynchronous, deterministic behaviour as the forward; d = 64 or
+ * 128; H a multiple of H_kv.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const void *dout, const float *lse, float *delta, void *dq,
+           void *dk, void *dv, int B, int H, int H_kv, int N, int d,
+           float scale, int causal, const int32_t *key_len,
+           const uint8_t *block_mask, hipStream_t stream);
+
 /* Query rows (Br) and key rows (Bc) per tile that fa_fwd_ex would use for
  * (dtype, d, block mask given or not, Br, Bc); writes them to *br_out /
  * *bc_out.  Returns FA_OK or FA_ERR_UNSUPPORTED_TILE /

@@ -117,6 +117,61 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     return FA_OK;
 }
 
+int backward(const void *q, const void *k, const void *v, const void *o, const void *dout,
+             const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int H, int Hkv,
+             int N, int d, float scale, int causal, const int32_t *key_len,
+             const uint8_t *block_mask, hipStream_t stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
+    if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    const uint64_t groups = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 15) / 16);
+    if (groups >= (1ull << 31)) return FA_ERR_INVALID_SHAPE;
+    const void *a16[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void *p : a16)
+        if (!aligned(p, 16)) return FA_ERR_MISALIGNED;
+    if (!aligned(lse, 4) || !aligned(delta, 4) || (key_len && !aligned(key_len, 4))) return FA_ERR_MISALIGNED;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const uint64_t qb = (uint64_t)B * H * N * d * 2, kvb = (uint64_t)B * Hkv * N * d * 2;
+    const uint64_t rb = (uint64_t)B * H * N * 4;
+    // outputs and the workspace must not overlap any input or each other
+    const struct { const void *p; uint64_t n; } ins[] = {{q, qb}, {k, kvb}, {v, kvb}, {o, qb}, {dout, qb},
+                                                         {lse, rb}};
+    const struct { const void *p; uint64_t n; } outs[] = {{dq, qb}, {dk, kvb}, {dv, kvb}, {delta, rb}};
+    for (const auto &w : outs) {
+        for (const auto &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
+        for (const auto &w2 : outs)
+            if (&w2 != &w && overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_INVALID_ARG;
+    }
+    fa::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.key_len = key_len;
+    a.block_mask = block_mask;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.Hkv = Hkv;
+    a.group = H / Hkv;
+    a.nkb = (N + 127) / 128;
+    a.scale = scale;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    const hipError_t err = fa::launch_bwd(a, d, causal ? 1 : 0, stream);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +210,14 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
                const uint8_t *block_mask, hipStream_t stream, int dtype, int Br, int Bc) {
     return forward(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
                    dtype, Br, Bc);
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int H, int H_kv,
+           int N, int d, float scale, int causal, const int32_t *key_len,
+           const uint8_t *block_mask, hipStream_t stream) {
+    return backward(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
+                    key_len, block_mask, stream);
 }
 
 int fa_tile_shape(int dtype, int d, int block_sparse, int Br, int Bc, int *br_out, int *bc_out) {

@@ -1,0 +1,482 @@
+// Exact-attention backward pass for gfx950: the gradients dQ, dK, dV of the
+// loss sum(dO * O), bf16 inputs and outputs, fp32 accumulation.
+//
+// The pages give the forward definition (page "Ch.04 Attention
+// optimisation: FlashAttention and sparse attention", mdooai.com, "Core
+// formula") and say the method's speed-ups are training speed-ups (page
+// "FlashAttention: Fast and Memory-Efficient Exact Attention with
+// IO-Awareness", ai-paper-library, Summary); the backward is the chain rule
+// applied to that definition, computed with the same IO-aware structure as
+// the forward: the probabilities are recomputed tile by tile from Q, K and
+// the forward's per-row log-sum-exp, never stored in HBM.  With
+// P = exp(S - LSE), dP = dO V^T, Delta_i = dO_i . O_i, dS = P * (dP - Delta):
+//     dV = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K.
+//
+// Three kernels:
+//  * bwd_delta: Delta_i = dO_i . O_i per query row (fp32, caller workspace).
+//  * bwd_dkdv: one workgroup per block of 32*NW keys of one key/value head;
+//    each wave keeps its 32 keys' K and V fragments and the dK^T, dV^T
+//    accumulators in registers and walks the query tiles (32 rows of Q and
+//    dO staged in LDS per step) of every query head that reads this
+//    key/value head.  Per step: S = Q K^T and dP = dO V^T (lane = key),
+//    then dV^T += dO^T P^T and dK^T += Q^T dS^T.
+//  * bwd_dq: one workgroup per 32*NW query rows; each wave keeps its rows'
+//    Q and dO fragments and the dQ^T accumulator in registers and walks the
+//    key tiles (32 keys of K and V staged in LDS per step).  Per step:
+//    S^T = K Q^T, dP^T = V dO^T (lane = query), then dQ^T += K^T dS^T.
+// Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics
+// and no fp32 scratch for dQ, and keeps the results deterministic.
+//
+// Layouts of the 32x32x16 bf16 matrix-core product (fp32 accumulate) are
+// those of the forward kernels: a product's 16 accumulator values per lane
+// are one column (lane % 32) and 16 rows; fed back as the B operand of the
+// next product, 8 of them give the 16-row reduction block with the row
+// permutation r(half, j) = 8*(j/4) + 4*half + j%4, which the transposed LDS
+// reads of the A operand reproduce.
+#include "fa_bf16_tiles.h"
+
+namespace fa {
+namespace {
+
+// Swizzle of the 16-byte slots of a tile row for tiles that are read both
+// as rows (ds_read_b128, 16 consecutive rows per 16-lane group) and
+// transposed (ds_read_b64_tr_b16, 4 rows x 4 slots per half-wave): for D =
+// 128, z(r) = 4*(r%4) + (r/4)%4 gives 16 distinct slots over any 16 aligned
+// rows and 16 distinct (row, slot) banks for a transposed read; for D = 64
+// (two rows per 256-byte bank line) the same on r/2.  z depends on r % 16
+// only.
+template <int D>
+__device__ __forceinline__ int zkv(int r) {
+    constexpr int RPL = 128 / D, G = D / 32;
+    const int x = r / RPL;
+    return 4 * (x % G) + (x / G) % 4;
+}
+
+// Element offset of logical slot `slot` of row r in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int slot) {
+    return r * D + ((slot ^ zkv<D>(r)) << 3);
+}
+
+template <int D>
+struct BwdGeom {
+    static constexpr int SLOTS = D / 8;
+    static constexpr int NQK = D / 16;  // 16-wide head-dim chunks
+    static constexpr int ND = D / 32;   // 32-wide output blocks
+    static constexpr int TILE = 32 * D; // elements per 32-row tile
+    static constexpr int NCOPY = TILE / 512;
+};
+
+// Copy rows [r0, r0 + 32) of a [.., D] bf16 matrix into a swizzled LDS tile
+// (rows >= rows_valid re-read the last valid row: their results are
+// masked).  The NW waves split the NCOPY 1 KiB copy instructions.
+template <int D, int NW>
+__device__ __forceinline__ void copy_rows(const __bf16 *G, int r0, int rows_valid, __bf16 *dst,
+                                          int wave, int lane) {
+    using Geo = BwdGeom<D>;
+#pragma unroll
+    for (int q0 = 0; q0 < Geo::NCOPY; q0 += NW) {
+        const int q = q0 + wave;
+        if (Geo::NCOPY % NW != 0 && q >= Geo::NCOPY) break;
+        const int ci = q * 64 + lane;
+        const int r = ci / Geo::SLOTS, p = ci % Geo::SLOTS;
+        const int row = min(r0 + r, rows_valid - 1);
+        const __bf16 *src = G + (int64_t)row * D + ((p ^ zkv<D>(r)) << 3);
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst + q * 512),
+                                         16, 0, 0);
+    }
+}
+
+// Per-lane offsets (elements, relative to a 16-row chunk) of the two 4-row
+// transposed reads that give the A fragment [32 columns of output block mb]
+// x [16 rows of the chunk] with the row permutation of the B fragments.
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&lo)[D / 32], int (&hi)[D / 32]) {
+    const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+        const int row = 4 * (g >> 1) + (li >> 2);
+        const int col = mb * 32 + 16 * (g & 1) + 4 * (li & 3);
+        lo[mb] = row * D + (((col >> 3) ^ zkv<D>(row)) << 3) + (col & 7);
+        hi[mb] = (row + 8) * D + (((col >> 3) ^ zkv<D>(row + 8)) << 3) + (col & 7);
+    }
+}
+
+__device__ __forceinline__ bf16x8_t read_tr8(const __bf16 *base, int lo, int hi) {
+    const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + lo));
+    const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + hi));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of accumulator value i of lane l in a 32x32 product block.
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// ---------------------------------------------------------------- Delta
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
+    // 16 lanes (D = 128) or 8 lanes (D = 64) per row, 8 elements each.
+    constexpr int LPR = D / 8;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+    const int part = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(
+            reinterpret_cast<const __bf16 *>(a.o) + row * D + part * 8);
+        const bf16x8_t y = *reinterpret_cast<const bf16x8_t *>(
+            reinterpret_cast<const __bf16 *>(a.dout) + row * D + part * 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fmaf((float)x[j], (float)y[j], acc);
+    }
+#pragma unroll
+    for (int s = LPR / 2; s > 0; s /= 2) acc += __shfl_xor(acc, s, LPR);
+    if (row < rows && part == 0) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) {
+    using Geo = BwdGeom<D>;
+    constexpr int NQK = Geo::NQK, ND = Geo::ND, BK = 32 * NW;
+    __shared__ __attribute__((aligned(1024))) __bf16 q_lds[2][Geo::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 do_lds[2][Geo::TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = a.N;
+    const int nkt = (N + BK - 1) / BK;
+    // Workgroup -> (batch, key/value head, key block); causal grids start
+    // with the key blocks that see the most query rows.
+    int id = blockIdx.x;
+    const int G = gridDim.x;
+    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
+    const int bkv = id / nkt;
+    int kt = id - bkv * nkt;
+    const int b = bkv / a.Hkv;
+    const int hkv = bkv - b * a.Hkv;
+    const int k0 = kt * BK, kw0 = k0 + wave * 32;
+
+    int kv_len = N;
+    if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
+    const int64_t kvhead = (int64_t)bkv * N * D;
+    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + kvhead;
+    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + kvhead;
+    const float c = a.scale_log2;
+    const bool wave_live = kw0 < kv_len;  // keys >= kv_len get zero gradients
+
+    // This wave's 32 keys as B operands: K^T and V^T fragments (lane: key
+    // lane % 32, head dims 16*ks + 8*(lane/32) .. +7).
+    const int key = kw0 + lane % 32;
+    bf16x8_t kf[NQK], vf[NQK];
+#pragma unroll
+    for (int ks = 0; ks < NQK; ++ks) {
+        u32x4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+        if (key < N) {
+            xk = *reinterpret_cast<const u32x4_t *>(K + (int64_t)key * D + ks * 16 + 8 * (lane / 32));
+            xv = *reinterpret_cast<const u32x4_t *>(V + (int64_t)key * D + ks * 16 + 8 * (lane / 32));
+        }
+        kf[ks] = __builtin_bit_cast(bf16x8_t, xk);
+        vf[ks] = __builtin_bit_cast(bf16x8_t, xv);
+    }
+    f32x16_t dk[ND], dv[ND];
+#pragma unroll
+    for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dk[mb][i] = dv[mb][i] = 0.f;
+
+    const int rbase = (lane % 32) * D + (((lane / 32) ^ zkv<D>(lane % 32)) << 3);
+    int trlo[ND], trhi[ND];
+    tr_offsets<D>(lane, trlo, trhi);
+
+    // Query tiles of 32 rows this key block can receive gradient from.
+    const int qt_first = CAUSAL ? k0 / 32 : 0;
+    const int nqt = (N + 31) / 32;
+    const int steps_per_head = nqt - qt_first;
+    // workgroup-uniform (every wave takes part in the copies and barriers)
+    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * a.group;
+    auto step_tile = [&](int s, int *hq, int *qt) {
+        const int g = s / steps_per_head;
+        *hq = b * a.H + hkv * a.group + g;
+        *qt = qt_first + (s - g * steps_per_head);
+    };
+    auto tile_active = [&](int qt) {
+        if (!a.block_mask) return true;
+        return a.block_mask[(int64_t)((qt * 32) >> 7) * a.nkb + (k0 >> 7)] != 0;
+    };
+    auto issue = [&](int s, int buf) {
+        int hq, qt;
+        step_tile(s, &hq, &qt);
+        const int64_t qhead = (int64_t)hq * N * D;
+        copy_rows<D, NW>(reinterpret_cast<const __bf16 *>(a.q) + qhead, qt * 32, N, q_lds[buf], wave, lane);
+        copy_rows<D, NW>(reinterpret_cast<const __bf16 *>(a.dout) + qhead, qt * 32, N, do_lds[buf], wave,
+                         lane);
+    };
+    // next active step at or after s (block mask), or nsteps
+    auto next_step = [&](int s) {
+        while (s < nsteps) {
+            int hq, qt;
+            step_tile(s, &hq, &qt);
+            if (tile_active(qt)) break;
+            ++s;
+        }
+        return s;
+    };
+
+    int s = next_step(0);
+    if (s < nsteps) issue(s, 0);
+    int buf = 0;
+    while (s < nsteps) {
+        const int sn = next_step(s + 1);
+        wait_copies();
+        __syncthreads();
+        if (sn < nsteps) issue(sn, buf ^ 1);
+        int hq, qt;
+        step_tile(s, &hq, &qt);
+        const int qs = qt * 32;
+        const __bf16 *Qs = q_lds[buf], *dOs = do_lds[buf];
+        // this wave's keys see some query of the tile
+        if (wave_live && (!CAUSAL || qs + 31 >= kw0)) {
+            // S = Q K^T and dP = dO V^T: D[m = query][n = key].
+            f32x16_t sacc = {}, dpacc = {};
+#pragma unroll
+            for (int ks = 0; ks < NQK; ++ks) {
+                const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(Qs + (rbase ^ (ks << 4)));
+                const bf16x8_t da = *reinterpret_cast<const bf16x8_t *>(dOs + (rbase ^ (ks << 4)));
+                sacc = mfma(qa, kf[ks], sacc);
+                dpacc = mfma(da, vf[ks], dpacc);
+            }
+            // LSE (base 2) and Delta of the 16 query rows this lane holds.
+            const int64_t rowbase = (int64_t)hq * N + qs;
+            float lse2[16], dl[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qi = qs + acc_row(i, lane);
+                const float l = qi < N ? a.lse[rowbase + acc_row(i, lane)] : kNegInf;
+                lse2[i] = l == kNegInf ? __builtin_inff() : l * 1.44269504088896341f;
+                dl[i] = qi < N ? a.delta[rowbase + acc_row(i, lane)] : 0.f;
+            }
+            const bool edge = (qs + 32 > N) || (kw0 + 32 > kv_len) || (CAUSAL && qs < kw0 + 31);
+            float p[16], ds[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                p[i] = fast_exp2(fmaf(sacc[i], c, -lse2[i]));
+                if (edge) {
+                    const int qi = qs + acc_row(i, lane);
+                    const bool ok = qi < N && key < kv_len && (!CAUSAL || key <= qi);
+                    p[i] = ok ? p[i] : 0.f;
+                }
+                ds[i] = p[i] * (dpacc[i] - dl[i]);
+            }
+            // dV^T += dO^T P^T and dK^T += Q^T dS^T over the two 16-row chunks.
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8_t pf, dsf;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pf[j] = (__bf16)p[8 * h + j];
+                    dsf[j] = (__bf16)ds[8 * h + j];
+                }
+#pragma unroll
+                for (int mb = 0; mb < ND; ++mb) {
+                    const bf16x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
+                    const bf16x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
+                    dv[mb] = mfma(dot, pf, dv[mb]);
+                    dk[mb] = mfma(qtr, dsf, dk[mb]);
+                }
+            }
+        }
+        s = sn;
+        buf ^= 1;
+    }
+
+    // dK = scale * dK^T^T, dV: lane holds key lane % 32, head dims
+    // 32*mb + 8*gg + 4*(lane/32) .. +3.
+    if (key < N) {
+        const float scale = a.scale;
+        __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + kvhead + (int64_t)key * D;
+        __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + kvhead + (int64_t)key * D;
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                bf16x4_t wk, wv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    wk[j] = (__bf16)(dk[mb][4 * gg + j] * scale);
+                    wv[j] = (__bf16)dv[mb][4 * gg + j];
+                }
+                *reinterpret_cast<bf16x4_t *>(dK + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
+                *reinterpret_cast<bf16x4_t *>(dV + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
+    using Geo = BwdGeom<D>;
+    constexpr int NQK = Geo::NQK, ND = Geo::ND, BR = 32 * NW;
+    __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2][Geo::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2][Geo::TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = a.N;
+    const int nqt = (N + BR - 1) / BR;
+    int bh, qt;
+    tile_of_block(nqt, CAUSAL, &bh, &qt);
+    const int b = bh / a.H;
+    const int64_t head = (int64_t)bh * N * D;
+    const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
+    const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
+    const __bf16 *dO = reinterpret_cast<const __bf16 *>(a.dout) + head;
+    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + kvhead;
+    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + kvhead;
+    const float c = a.scale_log2;
+
+    const int q0 = qt * BR, wq0 = q0 + wave * 32;
+    const int qrow = wq0 + lane % 32;
+    int kv_len = N;
+    if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
+    int kv_end = kv_len;
+    if (CAUSAL) kv_end = min(kv_end, q0 + BR);
+    const int ntiles = (kv_end + 31) / 32;
+
+    // This wave's 32 query rows as B operands: Q^T and dO^T fragments.
+    bf16x8_t qf[NQK], dof[NQK];
+#pragma unroll
+    for (int ks = 0; ks < NQK; ++ks) {
+        u32x4_t xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
+        if (qrow < N) {
+            xq = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
+            xd = *reinterpret_cast<const u32x4_t *>(dO + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
+        }
+        qf[ks] = __builtin_bit_cast(bf16x8_t, xq);
+        dof[ks] = __builtin_bit_cast(bf16x8_t, xd);
+    }
+    float lse2 = __builtin_inff(), dl = 0.f;
+    if (qrow < N) {
+        const float l = a.lse[(int64_t)bh * N + qrow];
+        lse2 = l == kNegInf ? __builtin_inff() : l * 1.44269504088896341f;
+        dl = a.delta[(int64_t)bh * N + qrow];
+    }
+    f32x16_t dq[ND];
+#pragma unroll
+    for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dq[mb][i] = 0.f;
+
+    const int rbase = (lane % 32) * D + (((lane / 32) ^ zkv<D>(lane % 32)) << 3);
+    int trlo[ND], trhi[ND];
+    tr_offsets<D>(lane, trlo, trhi);
+
+    // Key tiles of 32 keys, skipping 128-key blocks the mask turns off.
+    const uint8_t *mrow = a.block_mask ? a.block_mask + (int64_t)(q0 >> 7) * a.nkb : nullptr;
+    auto next_tile = [&](int t) {
+        if (mrow)
+            while (t < ntiles && mrow[(t * 32) >> 7] == 0) t = (((t * 32) >> 7) + 1) * 4;
+        return min(t, ntiles);
+    };
+    auto issue = [&](int t, int buf) {
+        copy_rows<D, NW>(K, t * 32, kv_len, k_lds[buf], wave, lane);
+        copy_rows<D, NW>(V, t * 32, kv_len, v_lds[buf], wave, lane);
+    };
+
+    int t = next_tile(0);
+    if (t < ntiles) issue(t, 0);
+    int buf = 0;
+    while (t < ntiles) {
+        const int tn = next_tile(t + 1);
+        wait_copies();
+        __syncthreads();
+        if (tn < ntiles) issue(tn, buf ^ 1);
+        const int kbase = t * 32;
+        const __bf16 *Ks = k_lds[buf], *Vs = v_lds[buf];
+        if (wq0 < N && (!CAUSAL || kbase <= wq0 + 31)) {
+            // S^T = K Q^T and dP^T = V dO^T: D[m = key][n = query].
+            f32x16_t sacc = {}, dpacc = {};
+#pragma unroll
+            for (int ks = 0; ks < NQK; ++ks) {
+                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + (rbase ^ (ks << 4)));
+                const bf16x8_t va = *reinterpret_cast<const bf16x8_t *>(Vs + (rbase ^ (ks << 4)));
+                sacc = mfma(ka, qf[ks], sacc);
+                dpacc = mfma(va, dof[ks], dpacc);
+            }
+            const bool edge = (kbase + 32 > kv_len) || (CAUSAL && kbase + 31 > wq0);
+            float ds[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float p = fast_exp2(fmaf(sacc[i], c, -lse2));
+                if (edge) {
+                    const int kj = kbase + acc_row(i, lane);
+                    const bool ok = kj < kv_len && (!CAUSAL || kj <= qrow);
+                    p = ok ? p : 0.f;
+                }
+                ds[i] = p * (dpacc[i] - dl);
+            }
+            // dQ^T += K^T dS^T over the two 16-key chunks.
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8_t dsf;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dsf[j] = (__bf16)ds[8 * h + j];
+#pragma unroll
+                for (int mb = 0; mb < ND; ++mb) {
+                    const bf16x8_t ktr = read_tr8(Ks + h * 16 * D, trlo[mb], trhi[mb]);
+                    dq[mb] = mfma(ktr, dsf, dq[mb]);
+                }
+            }
+        }
+        t = tn;
+        buf ^= 1;
+    }
+
+    if (qrow < N) {
+        const float scale = a.scale;
+        __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (int64_t)qrow * D;
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                bf16x4_t w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] = (__bf16)(dq[mb][4 * gg + j] * scale);
+                *reinterpret_cast<bf16x4_t *>(dQ + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
+    constexpr int NW = 4;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((bwd_delta<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((bwd_dkdv<D, NW, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64), 0,
+                       stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((bwd_dq<D, NW, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs &a, int d, int causal, hipStream_t stream) {
+    if (d == 64) return causal ? launch_bwd_impl<64, true>(a, stream) : launch_bwd_impl<64, false>(a, stream);
+    return causal ? launch_bwd_impl<128, true>(a, stream) : launch_bwd_impl<128, false>(a, stream);
+}
+
+}  // namespace fa

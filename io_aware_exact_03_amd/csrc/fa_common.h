@@ -68,7 +68,8 @@ __device__ __forceinline__ bool wave_any(bool pred) {
 // Key/value head read by query head bh = b*H + h: consecutive groups of
 // H/Hkv query heads share one key/value head (grouped-query attention;
 // Hkv = H is plain multi-head attention, Hkv = 1 multi-query attention).
-__device__ __forceinline__ int kv_head_of(int bh, const FwdArgs &a) {
+template <class Args>
+__device__ __forceinline__ int kv_head_of(int bh, const Args &a) {
     const int b = bh / a.H;
     return b * a.Hkv + (bh - b * a.H) / a.group;
 }

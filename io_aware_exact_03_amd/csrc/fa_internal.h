@@ -25,6 +25,24 @@ struct FwdArgs {
     float scale_log2;           // softmax scale * log2(e), fp32
 };
 
+// Everything the backward kernels need.
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;  // bf16 [B,H,N,d] (k, v: [B,Hkv,N,d])
+    const float *lse;                  // [B,H,N], natural log, from the forward
+    float *delta;                      // [B,H,N] workspace: dO_i . O_i
+    void *dq, *dk, *dv;                // bf16 outputs (dk, dv: [B,Hkv,N,d])
+    const int32_t *key_len;
+    const uint8_t *block_mask;
+    int B, H, N;
+    int Hkv, group;
+    int nkb;
+    float scale;       // softmax scale
+    float scale_log2;  // scale * log2(e)
+};
+
+// Enqueues the three backward kernels on `stream`.
+hipError_t launch_bwd(const BwdArgs &a, int d, int causal, hipStream_t stream);
+
 // Enqueues one forward pass on `stream`; returns the launch status.
 using Launcher = hipError_t (*)(const FwdArgs &, hipStream_t);
 

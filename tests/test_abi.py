@@ -26,8 +26,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study",
-                                           "fa_fwd_gqa", "fa_tile_shape", "fa_status_string",
-                                           "fa_last_hip_error"])
+                                           "fa_fwd_gqa", "fa_bwd", "fa_tile_shape",
+                                           "fa_status_string", "fa_last_hip_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -107,6 +107,32 @@ def test_study_order_validation(kw, status):
                           args["H"], args["N"], args["d"], args["scale"], args["causal"],
                           args["key_len"], args["block_mask"], args["stream"], args["dtype"],
                           args["Br"], args["Bc"], args["order"])
+    assert rc == status
+
+
+DO, LSEB, DELTA, DQ, DK, DV = 0x60000000, 0x70000000, 0x71000000, 0x72000000, 0x74000000, 0x76000000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(delta=None), 1),
+    (dict(dk=None), 1),
+    (dict(B=0), 2), (dict(H_kv=3), 2), (dict(N=0), 2),
+    (dict(d=96), 3),
+    (dict(dq=DQ + 8), 4), (dict(dout=DO + 2), 4), (dict(lse=LSEB + 2), 4),
+    (dict(scale=math.nan), 7),
+    (dict(dq=Q + 64), 7),                  # output over an input
+    (dict(dk=DV + 16), 7),                 # outputs overlapping each other
+    (dict(delta=LSEB + 4), 7),             # workspace over the logsumexp
+])
+def test_bwd_invalid_arguments_return_status_without_launch(kw, status):
+    args = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=LSEB, delta=DELTA, dq=DQ, dk=DK, dv=DV, B=2, H=4,
+                H_kv=2, N=100, d=64, scale=0.125, causal=0, key_len=None, block_mask=None,
+                stream=None)
+    args.update(kw)
+    lib = fa._load()
+    rc = lib.fa_bwd(*[args[n] for n in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv",
+                                         "B", "H", "H_kv", "N", "d", "scale", "causal", "key_len",
+                                         "block_mask", "stream")])
     assert rc == status
 
 

@@ -1,0 +1,117 @@
+"""GPU parity of the HIP backward pass (fa_bwd) against the FP64 backward
+oracle, which is the chain rule on the attention definition and is pinned by
+finite differences of the forward oracle (tests/test_oracle_bwd.py).
+
+Inputs are seeded bf16 Q, K, V and dO; O and LSE come from the library's own
+forward on the same inputs (as in training).  Bar: for each of dQ, dK, dV,
+max|g - g_ref| <= 2e-2 * max(1, max|g_ref|): the forward's bf16 tolerance
+taken relative to the gradient's scale (P and dS enter the products rounded
+to bf16, relative 2^-9 each, and every gradient is rounded to bf16 once).
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import io_aware_exact_03_amd as fa  # noqa: E402
+import oracle  # noqa: E402
+from workloads import random_qkv, band_global_block_mask  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).cuda()
+
+
+def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None, scale=None):
+    q, _, _, rng = random_qkv(B, H, N, d, seed, "bf16")
+    _, k, v, rng = random_qkv(B, H_kv, N, d, seed + 1, "bf16", rng=rng)
+    dout = rng.standard_normal(q.shape).astype(np.float32)
+    dout = dout.astype(np.float32)
+    scale = np.float32(1.0 / math.sqrt(d) if scale is None else scale)
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(dout)
+    dout_b = tdo.float().cpu().numpy()
+    kl = torch.from_numpy(np.asarray(key_len, dtype=np.int32)).cuda() if key_len is not None else None
+    bm = torch.from_numpy(np.asarray(block_mask, dtype=np.uint8)).cuda() if block_mask is not None else None
+    o, lse = fa.fwd(tq, tk, tv, causal=causal, key_len=kl, block_mask=bm, scale=float(scale))
+    dq = torch.full_like(tq, float("nan"))
+    dk = torch.full_like(tk, float("nan"))
+    dv = torch.full_like(tv, float("nan"))
+    fa.bwd(tq, tk, tv, o, tdo, lse, causal=causal, key_len=kl, block_mask=bm, scale=float(scale),
+           dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd_f64(q, k, v, dout_b, float(scale), causal,
+                                   None if key_len is None else np.asarray(key_len, dtype=np.int32),
+                                   None if block_mask is None else np.asarray(block_mask, dtype=np.uint8))
+    errs = {}
+    for name, g, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        g = g.double().cpu().numpy()
+        assert np.all(np.isfinite(g)), f"{name}: non-finite"
+        err = float(np.abs(g - r).max())
+        errs[name] = err
+        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        assert err <= bound, f"{name}: max|dg| = {err:.3e} > {bound:.3e}"
+    return errs
+
+
+def modes(N, seed):
+    rng = np.random.default_rng(seed)
+    nb = (N + 127) // 128
+    return {
+        "dense": dict(),
+        "causal": dict(causal=True),
+        "padded": dict(key_len=[max(1, N // 3), N]),
+        "blocks": dict(block_mask=band_global_block_mask(nb, rng, n_global=1)),
+        "all": dict(causal=True, key_len=[N, max(1, N - 5)],
+                    block_mask=band_global_block_mask(nb, rng, n_global=1)),
+    }
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 45, 300])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_bwd_modes(d, N, mode):
+    run_case(2, 2, 2, N, d, seed=70 + N + d, **modes(N, 71)[mode])
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 2), (4, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_grouped_heads(H, H_kv, causal):
+    run_case(1, H, H_kv, 200, 128, seed=72, causal=causal)
+
+
+def test_bwd_larger_causal():
+    run_case(1, 2, 2, 1000, 128, seed=73, causal=True)
+
+
+def test_bwd_fully_masked_batch_entry():
+    errs = run_case(2, 2, 2, 150, 64, seed=74, key_len=[0, 150])
+    assert all(e < 1 for e in errs.values())
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_bwd_nonstandard_scales(scale):
+    run_case(1, 2, 2, 130, 64, seed=75, causal=True, scale=scale)
+
+
+def test_bwd_deterministic():
+    q, k, v, rng = random_qkv(1, 2, 257, 128, 76, "bf16")
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    tdo = dev(rng.standard_normal(q.shape).astype(np.float32))
+    o, lse = fa.fwd(tq, tk, tv, causal=True)
+    a = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True)
+    b = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
