@@ -16,9 +16,9 @@
 //  * bwd_delta: Delta_i = dO_i . O_i per query row (fp32, caller workspace).
 //  * bwd_dkdv: one workgroup per block of 32*NW keys of one key/value head;
 //    each wave keeps its 32 keys' K and V fragments and the dK^T, dV^T
-//    accumulators in registers and walks the query tiles (32 rows of Q and
-//    dO staged in LDS per step) of every query head that reads this
-//    key/value head.  Per step: S = Q K^T and dP = dO V^T (lane = key),
+//    accumulators in registers and walks the query tiles (32*QT rows of Q
+//    and dO, with their LSE and Delta, staged in LDS per step) of every
+//    query head that reads this key/value head.  Per step: S = Q K^T and dP = dO V^T (lane = key),
 //    then dV^T += dO^T P^T and dK^T += Q^T dS^T.
 //  * bwd_dq: one workgroup per 32*NW query rows; each wave keeps its rows'
 //    Q and dO fragments and the dQ^T accumulator in registers and walks the
@@ -67,19 +67,19 @@ struct BwdGeom {
     static constexpr int NCOPY = TILE / 512;
 };
 
-// Copy rows [r0, r0 + 32) of a [.., D] bf16 matrix into a swizzled LDS tile
-// (rows >= rows_valid re-read the last valid row: their results are
-// masked).  The NW waves split the NCOPY 1 KiB copy instructions.
-template <int D, int NW>
+// Copy rows [r0, r0 + ROWS) of a [.., D] bf16 matrix into a swizzled LDS
+// tile (rows >= rows_valid re-read the last valid row: their results are
+// masked).  The NW waves split the 1 KiB copy instructions.
+template <int D, int NW, int ROWS = 32>
 __device__ __forceinline__ void copy_rows(const __bf16 *G, int r0, int rows_valid, __bf16 *dst,
                                           int wave, int lane) {
-    using Geo = BwdGeom<D>;
+    constexpr int SLOTS = D / 8, NCOPY = ROWS * D / 512;
 #pragma unroll
-    for (int q0 = 0; q0 < Geo::NCOPY; q0 += NW) {
+    for (int q0 = 0; q0 < NCOPY; q0 += NW) {
         const int q = q0 + wave;
-        if (Geo::NCOPY % NW != 0 && q >= Geo::NCOPY) break;
+        if (NCOPY % NW != 0 && q >= NCOPY) break;
         const int ci = q * 64 + lane;
-        const int r = ci / Geo::SLOTS, p = ci % Geo::SLOTS;
+        const int r = ci / SLOTS, p = ci % SLOTS;
         const int row = min(r0 + r, rows_valid - 1);
         const __bf16 *src = G + (int64_t)row * D + ((p ^ zkv<D>(r)) << 3);
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst + q * 512),
@@ -140,12 +140,16 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int QT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) {
     using Geo = BwdGeom<D>;
-    constexpr int NQK = Geo::NQK, ND = Geo::ND, BK = 32 * NW;
-    __shared__ __attribute__((aligned(1024))) __bf16 q_lds[2][Geo::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 do_lds[2][Geo::TILE];
+    constexpr int NQK = Geo::NQK, ND = Geo::ND, BK = 32 * NW, BQ = 32 * QT;
+    static_assert(128 % BQ == 0, "a query tile lies inside one 128-row mask block");
+    // Q and dO tiles of BQ rows, and the tile's LSE and Delta (BQ floats
+    // each, LSE first), double-buffered.
+    __shared__ __attribute__((aligned(1024))) __bf16 q_lds[2][BQ * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 do_lds[2][BQ * D];
+    __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * BQ];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,9 +198,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) 
     int trlo[ND], trhi[ND];
     tr_offsets<D>(lane, trlo, trhi);
 
-    // Query tiles of 32 rows this key block can receive gradient from.
-    const int qt_first = CAUSAL ? k0 / 32 : 0;
-    const int nqt = (N + 31) / 32;
+    // Query tiles of BQ rows this key block can receive gradient from.
+    const int qt_first = CAUSAL ? k0 / BQ : 0;
+    const int nqt = (N + BQ - 1) / BQ;
     const int steps_per_head = nqt - qt_first;
     // workgroup-uniform (every wave takes part in the copies and barriers)
     const int nsteps = k0 >= kv_len ? 0 : steps_per_head * a.group;
@@ -207,15 +211,25 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) 
     };
     auto tile_active = [&](int qt) {
         if (!a.block_mask) return true;
-        return a.block_mask[(int64_t)((qt * 32) >> 7) * a.nkb + (k0 >> 7)] != 0;
+        return a.block_mask[(int64_t)((qt * BQ) >> 7) * a.nkb + (k0 >> 7)] != 0;
     };
     auto issue = [&](int s, int buf) {
         int hq, qt;
         step_tile(s, &hq, &qt);
         const int64_t qhead = (int64_t)hq * N * D;
-        copy_rows<D, NW>(reinterpret_cast<const __bf16 *>(a.q) + qhead, qt * 32, N, q_lds[buf], wave, lane);
-        copy_rows<D, NW>(reinterpret_cast<const __bf16 *>(a.dout) + qhead, qt * 32, N, do_lds[buf], wave,
-                         lane);
+        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.q) + qhead, qt * BQ, N, q_lds[buf], wave,
+                             lane);
+        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.dout) + qhead, qt * BQ, N, do_lds[buf],
+                             wave, lane);
+        // LSE and Delta of the tile's rows (4 bytes per lane; clamped rows
+        // past N are masked).
+        if (wave * 64 < 2 * BQ) {
+            const int idx = wave * 64 + lane;  // 0 .. 2*BQ-1
+            const int r = min(qt * BQ + (idx % BQ), N - 1);
+            const float *src = (idx < BQ ? a.lse : a.delta) + (int64_t)hq * N + r;
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(&ld_lds[buf][wave * 64]),
+                                             4, 0, 0);
+        }
     };
     // next active step at or after s (block mask), or nsteps
     auto next_step = [&](int s) {
@@ -238,56 +252,62 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) 
         if (sn < nsteps) issue(sn, buf ^ 1);
         int hq, qt;
         step_tile(s, &hq, &qt);
-        const int qs = qt * 32;
-        const __bf16 *Qs = q_lds[buf], *dOs = do_lds[buf];
-        // this wave's keys see some query of the tile
-        if (wave_live && (!CAUSAL || qs + 31 >= kw0)) {
-            // S = Q K^T and dP = dO V^T: D[m = query][n = key].
-            f32x16_t sacc = {}, dpacc = {};
+        const int qs0 = qt * BQ;
+        const float *lds_l = ld_lds[buf];
 #pragma unroll
-            for (int ks = 0; ks < NQK; ++ks) {
-                const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(Qs + (rbase ^ (ks << 4)));
-                const bf16x8_t da = *reinterpret_cast<const bf16x8_t *>(dOs + (rbase ^ (ks << 4)));
-                sacc = mfma(qa, kf[ks], sacc);
-                dpacc = mfma(da, vf[ks], dpacc);
-            }
-            // LSE (base 2) and Delta of the 16 query rows this lane holds.
-            const int64_t rowbase = (int64_t)hq * N + qs;
-            float lse2[16], dl[16];
+        for (int hq32 = 0; hq32 < QT; ++hq32) {
+            const int qs = qs0 + 32 * hq32;
+            const __bf16 *Qs = q_lds[buf] + hq32 * 32 * D, *dOs = do_lds[buf] + hq32 * 32 * D;
+            // this wave's keys see some query of these 32 rows
+            if (wave_live && (!CAUSAL || qs + 31 >= kw0)) {
+                // S = Q K^T and dP = dO V^T: D[m = query][n = key].
+                f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int qi = qs + acc_row(i, lane);
-                const float l = qi < N ? a.lse[rowbase + acc_row(i, lane)] : kNegInf;
-                lse2[i] = l == kNegInf ? __builtin_inff() : l * 1.44269504088896341f;
-                dl[i] = qi < N ? a.delta[rowbase + acc_row(i, lane)] : 0.f;
-            }
-            const bool edge = (qs + 32 > N) || (kw0 + 32 > kv_len) || (CAUSAL && qs < kw0 + 31);
-            float p[16], ds[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p[i] = fast_exp2(fmaf(sacc[i], c, -lse2[i]));
-                if (edge) {
-                    const int qi = qs + acc_row(i, lane);
-                    const bool ok = qi < N && key < kv_len && (!CAUSAL || key <= qi);
-                    p[i] = ok ? p[i] : 0.f;
+                for (int ks = 0; ks < NQK; ++ks) {
+                    const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(Qs + (rbase ^ (ks << 4)));
+                    const bf16x8_t da = *reinterpret_cast<const bf16x8_t *>(dOs + (rbase ^ (ks << 4)));
+                    sacc = mfma(qa, kf[ks], sacc);
+                    dpacc = mfma(da, vf[ks], dpacc);
                 }
-                ds[i] = p[i] * (dpacc[i] - dl[i]);
-            }
-            // dV^T += dO^T P^T and dK^T += Q^T dS^T over the two 16-row chunks.
+                const bool edge = (qs + 32 > N) || (kw0 + 32 > kv_len) || (CAUSAL && qs < kw0 + 31);
+                // P and dS in place; this lane's 16 rows are 4 groups of 4
+                // consecutive query rows: LSE and Delta as float4 LDS reads.
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bf16x8_t pf, dsf;
+                for (int gi = 0; gi < 4; ++gi) {
+                    const int r4 = 32 * hq32 + 8 * gi + 4 * (lane >> 5);
+                    const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lds_l + r4);
+                    const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(lds_l + BQ + r4);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    pf[j] = (__bf16)p[8 * h + j];
-                    dsf[j] = (__bf16)ds[8 * h + j];
+                    for (int j = 0; j < 4; ++j) {
+                        const int i = 4 * gi + j;
+                        // a row with no allowed key (LSE = -inf) gets p = 0
+                        const float l2 = l4[j] == kNegInf ? __builtin_inff() : l4[j] * 1.44269504088896341f;
+                        float p = fast_exp2(fmaf(sacc[i], c, -l2));
+                        if (edge) {
+                            const int qi = qs + acc_row(i, lane);
+                            const bool ok = qi < N && key < kv_len && (!CAUSAL || key <= qi);
+                            p = ok ? p : 0.f;
+                        }
+                        dpacc[i] = p * (dpacc[i] - d4[j]);
+                        sacc[i] = p;
+                    }
                 }
+                // dV^T += dO^T P^T and dK^T += Q^T dS^T over the two 16-row chunks.
 #pragma unroll
-                for (int mb = 0; mb < ND; ++mb) {
-                    const bf16x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
-                    const bf16x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
-                    dv[mb] = mfma(dot, pf, dv[mb]);
-                    dk[mb] = mfma(qtr, dsf, dk[mb]);
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8_t pf, dsf;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        pf[j] = (__bf16)sacc[8 * h + j];
+                        dsf[j] = (__bf16)dpacc[8 * h + j];
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < ND; ++mb) {
+                        const bf16x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
+                        const bf16x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
+                        dv[mb] = mfma(dot, pf, dv[mb]);
+                        dk[mb] = mfma(qtr, dsf, dk[mb]);
+                    }
                 }
             }
         }
@@ -295,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) 
         buf ^= 1;
     }
 
-    // dK = scale * dK^T^T, dV: lane holds key lane % 32, head dims
+    // dK = scale * (dK^T)^T, dV: lane holds key lane % 32, head dims
     // 32*mb + 8*gg + 4*(lane/32) .. +3.
     if (key < N) {
         const float scale = a.scale;
@@ -462,8 +482,11 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((bwd_dkdv<D, NW, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64), 0,
-                       stream, a);
+    // query rows per step: 128 for d = 128 (512-register mode), 64 for d = 64
+    // (two workgroups per CU; 128 rows would spill)
+    constexpr int QT = D == 128 ? 4 : 2;
+    hipLaunchKernelGGL((bwd_dkdv<D, NW, QT, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64),
+                       0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
