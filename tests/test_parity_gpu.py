@@ -174,6 +174,24 @@ def test_large_workloads_sampled_rows(name):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
+@pytest.mark.parametrize("N,d,causal", [(65536, 128, True), (65533, 64, False), (40000, 128, True)])
+def test_very_long_sequences_sampled_rows(N, d, causal):
+    """Single-head sequences up to 64K tokens (the longest context the
+    FlashAttention summary page reports, Path-256), ragged lengths included;
+    checked on sampled rows, with the tile-study kernel on the same input."""
+    inp = custom(1, 1, N, d, seed=90 + d, causal=causal, amp=0.5)
+    rows = sample_rows(1, 1, N, seed=91, per_head=24)
+    o_ref, lse_ref = oracle.attention_rows_f64(inp["q"], inp["k"], inp["v"], rows,
+                                               float(inp["scale"]), causal, None, None, 128)
+    o, lse = run(inp)
+    check(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, TOL_BF16, f"N={N} d={d}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    if d == 128:
+        o, lse = run(inp, Br=64, Bc=128)
+        check(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, TOL_BF16,
+              f"N={N} tile study")
+
+
 @pytest.mark.parametrize("Br", [16, 32, 64, 128])
 @pytest.mark.parametrize("Bc", [16, 32, 64, 128])
 def test_tile_sweep_slice(Br, Bc):
