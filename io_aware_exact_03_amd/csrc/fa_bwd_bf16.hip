@@ -19,7 +19,11 @@
 //    accumulators in registers and walks the query tiles (32*QT rows of Q
 //    and dO, with their LSE and Delta, staged in LDS per step) of every
 //    query head that reads this key/value head.  Per step: S = Q K^T and dP = dO V^T (lane = key),
-//    then dV^T += dO^T P^T and dK^T += Q^T dS^T.
+//    then dV^T += dO^T P^T and dK^T += Q^T dS^T.  Used for d = 64.
+//  * bwd_dkdv_pair (d = 128): the same product chain with 8 waves per 128
+//    keys, two waves per 32 keys splitting each 64-row query tile, so that a
+//    wave's registers fit two waves per SIMD; the pair's partial dK, dV are
+//    added through LDS at the end.
 //  * bwd_dq: one workgroup per 32*NW query rows; each wave keeps its rows'
 //    Q and dO fragments and the dQ^T accumulator in registers and walks the
 //    key tiles (32 keys of K and V staged in LDS per step).  Per step:
@@ -337,6 +341,212 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) 
     }
 }
 
+// dK, dV with two waves per key group (d = 128, two waves per SIMD): a
+// workgroup of 8 waves owns 128 keys; waves w and w+4 hold the same 32 keys
+// and take the two 32-row halves of each 64-row query tile, so each keeps only
+// its K fragments and its dK^T, dV^T accumulators in registers (V fragments
+// come from the key block's K/V tiles, loaded into LDS once).  The two
+// partial sums of each key group are added through LDS at the end.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair(BwdArgs a) {
+    using Geo = BwdGeom<D>;
+    constexpr int NQK = Geo::NQK, ND = Geo::ND, NW = 8, BK = 128, BQ = 64;
+    constexpr int KV_BYTES = BK * D * 2, T_BYTES = BQ * D * 2;
+    constexpr int RED_BYTES = 4 * 2 * ND * 16 * 64 * 4;  // 4 groups x (dk, dv) x 16*ND floats x 64 lanes
+    constexpr int POOL = 2 * KV_BYTES + 4 * T_BYTES > RED_BYTES ? 2 * KV_BYTES + 4 * T_BYTES : RED_BYTES;
+    __shared__ __attribute__((aligned(1024))) char pool[POOL];
+    __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * BQ];
+    __bf16 *const k_lds = reinterpret_cast<__bf16 *>(pool);
+    __bf16 *const v_lds = reinterpret_cast<__bf16 *>(pool + KV_BYTES);
+    auto q_lds = [&](int buf) { return reinterpret_cast<__bf16 *>(pool + 2 * KV_BYTES + buf * T_BYTES); };
+    auto do_lds = [&](int buf) { return reinterpret_cast<__bf16 *>(pool + 2 * KV_BYTES + (2 + buf) * T_BYTES); };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3, qh = wave >> 2;
+    const int N = a.N;
+    const int nkt = (N + BK - 1) / BK;
+    int id = blockIdx.x;
+    const int G = gridDim.x;
+    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
+    const int bkv = id / nkt;
+    const int kt = id - bkv * nkt;
+    const int b = bkv / a.Hkv;
+    const int hkv = bkv - b * a.Hkv;
+    const int k0 = kt * BK, kw0 = k0 + kg * 32;
+
+    int kv_len = N;
+    if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
+    const int64_t kvhead = (int64_t)bkv * N * D;
+    const float c = a.scale_log2;
+    const bool wave_live = kw0 < kv_len;
+    const int key = kw0 + lane % 32;
+
+    // The key block's K and V rows into LDS (rows past N re-read row N-1).
+    copy_rows<D, NW, BK>(reinterpret_cast<const __bf16 *>(a.k) + kvhead, k0, N, k_lds, wave, lane);
+    copy_rows<D, NW, BK>(reinterpret_cast<const __bf16 *>(a.v) + kvhead, k0, N, v_lds, wave, lane);
+
+    const int rbase = (lane % 32) * D + (((lane / 32) ^ zkv<D>(lane % 32)) << 3);
+    int trlo[ND], trhi[ND];
+    tr_offsets<D>(lane, trlo, trhi);
+    f32x16_t dk[ND], dv[ND];
+#pragma unroll
+    for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dk[mb][i] = dv[mb][i] = 0.f;
+
+    const int qt_first = CAUSAL ? k0 / BQ : 0;
+    const int nqt = (N + BQ - 1) / BQ;
+    const int steps_per_head = nqt - qt_first;
+    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * a.group;
+    auto step_tile = [&](int s, int *hq, int *qt) {
+        const int g = s / steps_per_head;
+        *hq = b * a.H + hkv * a.group + g;
+        *qt = qt_first + (s - g * steps_per_head);
+    };
+    auto tile_active = [&](int qt) {
+        if (!a.block_mask) return true;
+        return a.block_mask[(int64_t)((qt * BQ) >> 7) * a.nkb + (k0 >> 7)] != 0;
+    };
+    auto issue = [&](int s, int buf) {
+        int hq, qt;
+        step_tile(s, &hq, &qt);
+        const int64_t qhead = (int64_t)hq * N * D;
+        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.q) + qhead, qt * BQ, N, q_lds(buf), wave, lane);
+        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.dout) + qhead, qt * BQ, N, do_lds(buf), wave,
+                             lane);
+        if (wave < 2) {
+            const int idx = wave * 64 + lane;
+            const int r = min(qt * BQ + (idx % BQ), N - 1);
+            const float *src = (idx < BQ ? a.lse : a.delta) + (int64_t)hq * N + r;
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(&ld_lds[buf][wave * 64]),
+                                             4, 0, 0);
+        }
+    };
+    auto next_step = [&](int s) {
+        while (s < nsteps) {
+            int hq, qt;
+            step_tile(s, &hq, &qt);
+            if (tile_active(qt)) break;
+            ++s;
+        }
+        return s;
+    };
+
+    int s = next_step(0);
+    if (s < nsteps) issue(s, 0);
+    wait_copies();
+    __syncthreads();
+    // This wave's K^T fragments (B operand of S = Q K^T), kept in registers.
+    bf16x8_t kf[NQK];
+    const __bf16 *kg_k = k_lds + kg * 32 * D, *kg_v = v_lds + kg * 32 * D;
+#pragma unroll
+    for (int ks = 0; ks < NQK; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t *>(kg_k + (rbase ^ (ks << 4)));
+
+    int buf = 0;
+    while (s < nsteps) {
+        const int sn = next_step(s + 1);
+        wait_copies();
+        __syncthreads();
+        if (sn < nsteps) issue(sn, buf ^ 1);
+        int hq, qt;
+        step_tile(s, &hq, &qt);
+        const int qs = qt * BQ + 32 * qh;
+        const __bf16 *Qs = q_lds(buf) + qh * 32 * D, *dOs = do_lds(buf) + qh * 32 * D;
+        const float *lds_l = ld_lds[buf];
+        if (wave_live && (!CAUSAL || qs + 31 >= kw0)) {
+            f32x16_t sacc = {}, dpacc = {};
+#pragma unroll
+            for (int ks = 0; ks < NQK; ++ks) {
+                const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(Qs + (rbase ^ (ks << 4)));
+                const bf16x8_t da = *reinterpret_cast<const bf16x8_t *>(dOs + (rbase ^ (ks << 4)));
+                const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(kg_v + (rbase ^ (ks << 4)));
+                sacc = mfma(qa, kf[ks], sacc);
+                dpacc = mfma(da, vb, dpacc);
+            }
+            const bool edge = (qs + 32 > N) || (kw0 + 32 > kv_len) || (CAUSAL && qs < kw0 + 31);
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int r4 = 32 * qh + 8 * gi + 4 * (lane >> 5);
+                const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lds_l + r4);
+                const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(lds_l + BQ + r4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 4 * gi + j;
+                    const float l2 = l4[j] == kNegInf ? __builtin_inff() : l4[j] * 1.44269504088896341f;
+                    float p = fast_exp2(fmaf(sacc[i], c, -l2));
+                    if (edge) {
+                        const int qi = qs + acc_row(i, lane);
+                        const bool ok = qi < N && key < kv_len && (!CAUSAL || key <= qi);
+                        p = ok ? p : 0.f;
+                    }
+                    dpacc[i] = p * (dpacc[i] - d4[j]);
+                    sacc[i] = p;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8_t pf, dsf;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    pf[j] = (__bf16)sacc[8 * h + j];
+                    dsf[j] = (__bf16)dpacc[8 * h + j];
+                }
+#pragma unroll
+                for (int mb = 0; mb < ND; ++mb) {
+                    const bf16x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
+                    const bf16x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
+                    dv[mb] = mfma(dot, pf, dv[mb]);
+                    dk[mb] = mfma(qtr, dsf, dk[mb]);
+                }
+            }
+        }
+        s = sn;
+        buf ^= 1;
+    }
+
+    // Add the two halves' partial sums: the upper waves park theirs in LDS.
+    wait_copies();
+    __syncthreads();
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(pool) + (int64_t)kg * (2 * ND * 4) * 64;
+    if (qh == 1) {
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                f32x4_t xk, xv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xk[j] = dk[mb][4 * gg + j];
+                    xv[j] = dv[mb][4 * gg + j];
+                }
+                red[((2 * mb) * 4 + gg) * 64 + lane] = xk;
+                red[((2 * mb + 1) * 4 + gg) * 64 + lane] = xv;
+            }
+    }
+    __syncthreads();
+    if (qh == 0 && key < N) {
+        const float scale = a.scale;
+        __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + kvhead + (int64_t)key * D;
+        __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + kvhead + (int64_t)key * D;
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const f32x4_t xk = red[((2 * mb) * 4 + gg) * 64 + lane];
+                const f32x4_t xv = red[((2 * mb + 1) * 4 + gg) * 64 + lane];
+                bf16x4_t wk, wv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    wk[j] = (__bf16)((dk[mb][4 * gg + j] + xk[j]) * scale);
+                    wv[j] = (__bf16)(dv[mb][4 * gg + j] + xv[j]);
+                }
+                *reinterpret_cast<bf16x4_t *>(dK + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
+                *reinterpret_cast<bf16x4_t *>(dV + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
+            }
+    }
+}
+
 // ---------------------------------------------------------------- dQ
 
 template <int D, int NW, bool CAUSAL>
@@ -485,8 +695,12 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     // query rows per step: 128 for d = 128 (512-register mode), 64 for d = 64
     // (two workgroups per CU; 128 rows would spill)
     constexpr int QT = D == 128 ? 4 : 2;
-    hipLaunchKernelGGL((bwd_dkdv<D, NW, QT, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64),
-                       0, stream, a);
+    if constexpr (D == 128)
+        hipLaunchKernelGGL((bwd_dkdv_pair<D, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((bwd_dkdv<D, NW, QT, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64),
+                           0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
