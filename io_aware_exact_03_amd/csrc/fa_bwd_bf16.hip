@@ -19,15 +19,17 @@
 //    accumulators in registers and walks the query tiles (32*QT rows of Q
 //    and dO, with their LSE and Delta, staged in LDS per step) of every
 //    query head that reads this key/value head.  Per step: S = Q K^T and dP = dO V^T (lane = key),
-//    then dV^T += dO^T P^T and dK^T += Q^T dS^T.  Used for d = 64.
-//  * bwd_dkdv_pair (d = 128): the same product chain with 8 waves per 128
-//    keys, two waves per 32 keys splitting each 64-row query tile, so that a
-//    wave's registers fit two waves per SIMD; the pair's partial dK, dV are
-//    added through LDS at the end.
+//    then dV^T += dO^T P^T and dK^T += Q^T dS^T.  Used for d = 64 without
+//    the causal mask.
+//  * bwd_dkdv_pair (d = 128, and causal d = 64): the same product chain with
+//    8 waves per 128 keys, two waves per 32 keys splitting each 64-row query
+//    tile, so that a wave's registers fit two waves per SIMD at d = 128; the
+//    pair's partial dK, dV are added through LDS at the end.
 //  * bwd_dq: one workgroup per 32*NW query rows; each wave keeps its rows'
 //    Q and dO fragments and the dQ^T accumulator in registers and walks the
-//    key tiles (32 keys of K and V staged in LDS per step).  Per step:
-//    S^T = K Q^T, dP^T = V dO^T (lane = query), then dQ^T += K^T dS^T.
+//    key tiles (64 keys of K and V staged in LDS per step, taken as two
+//    32-key chunks).  Per chunk: S^T = K Q^T, dP^T = V dO^T (lane = query),
+//    then dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics
 // and no fp32 scratch for dQ, and keeps the results deterministic.
 //
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) 
 // come from the key block's K/V tiles, loaded into LDS once).  The two
 // partial sums of each key group are added through LDS at the end.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair(BwdArgs a) {
+__global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a) {
     using Geo = BwdGeom<D>;
     constexpr int NQK = Geo::NQK, ND = Geo::ND, NW = 8, BK = 128, BQ = 64;
     constexpr int KV_BYTES = BK * D * 2, T_BYTES = BQ * D * 2;
@@ -549,12 +551,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair(BwdArgs a) {
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int KT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     using Geo = BwdGeom<D>;
-    constexpr int NQK = Geo::NQK, ND = Geo::ND, BR = 32 * NW;
-    __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2][Geo::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2][Geo::TILE];
+    constexpr int NQK = Geo::NQK, ND = Geo::ND, BR = 32 * NW, BKT = 32 * KT;
+    static_assert(128 % BKT == 0, "a key step lies inside one 128-key mask block");
+    __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2][KT * Geo::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2][KT * Geo::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
     int kv_end = kv_len;
     if (CAUSAL) kv_end = min(kv_end, q0 + BR);
-    const int ntiles = (kv_end + 31) / 32;
+    const int ntiles = (kv_end + BKT - 1) / BKT;
 
     // This wave's 32 query rows as B operands: Q^T and dO^T fragments.
     bf16x8_t qf[NQK], dof[NQK];
@@ -607,16 +610,17 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     int trlo[ND], trhi[ND];
     tr_offsets<D>(lane, trlo, trhi);
 
-    // Key tiles of 32 keys, skipping 128-key blocks the mask turns off.
+    // Key steps of BKT keys (KT chunks of 32), skipping 128-key blocks the
+    // mask turns off.
     const uint8_t *mrow = a.block_mask ? a.block_mask + (int64_t)(q0 >> 7) * a.nkb : nullptr;
     auto next_tile = [&](int t) {
         if (mrow)
-            while (t < ntiles && mrow[(t * 32) >> 7] == 0) t = (((t * 32) >> 7) + 1) * 4;
+            while (t < ntiles && mrow[(t * BKT) >> 7] == 0) t = (((t * BKT) >> 7) + 1) * (128 / BKT);
         return min(t, ntiles);
     };
     auto issue = [&](int t, int buf) {
-        copy_rows<D, NW>(K, t * 32, kv_len, k_lds[buf], wave, lane);
-        copy_rows<D, NW>(V, t * 32, kv_len, v_lds[buf], wave, lane);
+        copy_rows<D, NW, BKT>(K, t * BKT, kv_len, k_lds[buf], wave, lane);
+        copy_rows<D, NW, BKT>(V, t * BKT, kv_len, v_lds[buf], wave, lane);
     };
 
     int t = next_tile(0);
@@ -627,40 +631,45 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
         wait_copies();
         __syncthreads();
         if (tn < ntiles) issue(tn, buf ^ 1);
-        const int kbase = t * 32;
-        const __bf16 *Ks = k_lds[buf], *Vs = v_lds[buf];
-        if (wq0 < N && (!CAUSAL || kbase <= wq0 + 31)) {
-            // S^T = K Q^T and dP^T = V dO^T: D[m = key][n = query].
-            f32x16_t sacc = {}, dpacc = {};
+        // one 32-key chunk at a time (unrolling lets the compiler hoist the
+        // next chunk's loads and spill)
+#pragma unroll 1
+        for (int kc = 0; kc < KT; ++kc) {
+            const int kbase = t * BKT + 32 * kc;
+            const __bf16 *Ks = k_lds[buf] + kc * Geo::TILE, *Vs = v_lds[buf] + kc * Geo::TILE;
+            if (wq0 < N && kbase < kv_end && (!CAUSAL || kbase <= wq0 + 31)) {
+                // S^T = K Q^T and dP^T = V dO^T: D[m = key][n = query].
+                f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
-            for (int ks = 0; ks < NQK; ++ks) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + (rbase ^ (ks << 4)));
-                const bf16x8_t va = *reinterpret_cast<const bf16x8_t *>(Vs + (rbase ^ (ks << 4)));
-                sacc = mfma(ka, qf[ks], sacc);
-                dpacc = mfma(va, dof[ks], dpacc);
-            }
-            const bool edge = (kbase + 32 > kv_len) || (CAUSAL && kbase + 31 > wq0);
-            float ds[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float p = fast_exp2(fmaf(sacc[i], c, -lse2));
-                if (edge) {
-                    const int kj = kbase + acc_row(i, lane);
-                    const bool ok = kj < kv_len && (!CAUSAL || kj <= qrow);
-                    p = ok ? p : 0.f;
+                for (int ks = 0; ks < NQK; ++ks) {
+                    const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + (rbase ^ (ks << 4)));
+                    const bf16x8_t va = *reinterpret_cast<const bf16x8_t *>(Vs + (rbase ^ (ks << 4)));
+                    sacc = mfma(ka, qf[ks], sacc);
+                    dpacc = mfma(va, dof[ks], dpacc);
                 }
-                ds[i] = p * (dpacc[i] - dl);
-            }
-            // dQ^T += K^T dS^T over the two 16-key chunks.
+                const bool edge = (kbase + 32 > kv_len) || (CAUSAL && kbase + 31 > wq0);
+                float ds[16];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                bf16x8_t dsf;
+                for (int i = 0; i < 16; ++i) {
+                    float p = fast_exp2(fmaf(sacc[i], c, -lse2));
+                    if (edge) {
+                        const int kj = kbase + acc_row(i, lane);
+                        const bool ok = kj < kv_len && (!CAUSAL || kj <= qrow);
+                        p = ok ? p : 0.f;
+                    }
+                    ds[i] = p * (dpacc[i] - dl);
+                }
+                // dQ^T += K^T dS^T over the two 16-key chunks.
 #pragma unroll
-                for (int j = 0; j < 8; ++j) dsf[j] = (__bf16)ds[8 * h + j];
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8_t dsf;
 #pragma unroll
-                for (int mb = 0; mb < ND; ++mb) {
-                    const bf16x8_t ktr = read_tr8(Ks + h * 16 * D, trlo[mb], trhi[mb]);
-                    dq[mb] = mfma(ktr, dsf, dq[mb]);
+                    for (int j = 0; j < 8; ++j) dsf[j] = (__bf16)ds[8 * h + j];
+#pragma unroll
+                    for (int mb = 0; mb < ND; ++mb) {
+                        const bf16x8_t ktr = read_tr8(Ks + h * 16 * D, trlo[mb], trhi[mb]);
+                        dq[mb] = mfma(ktr, dsf, dq[mb]);
+                    }
                 }
             }
         }
@@ -695,7 +704,7 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     // query rows per step: 128 for d = 128 (512-register mode), 64 for d = 64
     // (two workgroups per CU; 128 rows would spill)
     constexpr int QT = D == 128 ? 4 : 2;
-    if constexpr (D == 128)
+    if constexpr (D == 128 || CAUSAL)
         hipLaunchKernelGGL((bwd_dkdv_pair<D, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0, stream,
                            a);
     else
@@ -704,7 +713,8 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((bwd_dq<D, NW, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream,
+    constexpr int KT = 2;
+    hipLaunchKernelGGL((bwd_dq<D, NW, KT, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream,
                        a);
     return hipGetLastError();
 }
