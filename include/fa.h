@@ -124,7 +124,7 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               hipStream_t stream, int dtype, int Br, int Bc);
 
 /* Key-tile visit orders for fa_fwd_study. */
-enum { FA_ORDER_ASCENDING = 0, FA_ORDER_DESCENDING = 1 };
+enum { FA_ORDER_ASCENDING = 0, FA_ORDER_DESCENDING = 1, FA_ORDER_SHUFFLED = 2 };
 
 /*
  * Tile-order control for the deviation study: the page "Is Flash Attention
@@ -132,11 +132,15 @@ enum { FA_ORDER_ASCENDING = 0, FA_ORDER_DESCENDING = 1 };
  * blocks/tiles are processed besides their sizes, and asks libraries to
  * expose such settings (section 6).  Same arguments as fa_fwd_ex plus
  *   tile_order : FA_ORDER_ASCENDING (key tiles 0, 1, ...; what every other
- *                entry point does) or FA_ORDER_DESCENDING (last key tile
- *                first).  Other values: FA_ERR_INVALID_ARG.
+ *                entry point does), FA_ORDER_DESCENDING (last key tile
+ *                first) or FA_ORDER_SHUFFLED (a fixed permutation: of a
+ *                workgroup's n key tiles, visit i goes to tile
+ *                (a*i + n/2) mod n, a the smallest integer >= round(0.618*n)
+ *                coprime to n; tiles the block mask turns off are skipped).
+ *                Other values: FA_ERR_INVALID_ARG.
  * The result is the same attention up to rounding; only the order of the
- * running-maximum/rescale steps changes.  FA_ORDER_DESCENDING runs on the
- * tile-study kernels only (bf16, d = 128, explicit Br, Bc in
+ * running-maximum/rescale steps changes.  Orders other than ascending run
+ * on the tile-study kernels only (bf16, d = 128, explicit Br, Bc in
  * {16, 32, 64, 128}); other tiles return FA_ERR_UNSUPPORTED_TILE.
  */
 int fa_fwd_study(const void *q, const void *k, const void *v, void *o, float *lse,

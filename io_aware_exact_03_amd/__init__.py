@@ -14,7 +14,7 @@ import math
 import os
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_bwd", "bwd",
-           "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING",
+           "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING", "ORDER_SHUFFLED",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
            "DTYPE_BF16", "DTYPE_F32", "DTYPE_F16", "MASK_BLOCK"]
 
@@ -24,6 +24,7 @@ DTYPE_F32 = 1
 DTYPE_F16 = 2
 ORDER_ASCENDING = 0
 ORDER_DESCENDING = 1
+ORDER_SHUFFLED = 2
 MASK_BLOCK = 128
 
 FA_OK = 0
@@ -155,7 +156,8 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
     1/sqrt(d).  Br/Bc = 0 selects the tuned tile.  Returns (o, lse) with o like
     q and lse float32 [B, H, N]; `out`/`lse` may be passed preallocated, and
     lse=False skips the logsumexp (returned as None).  tile_order =
-    ORDER_DESCENDING visits key tiles last-first (tile-study kernels only).
+    ORDER_DESCENDING visits key tiles last-first, ORDER_SHUFFLED in a fixed
+    permutation (tile-study kernels only).
     """
     import torch
     if q.dtype != k.dtype or q.dtype != v.dtype:

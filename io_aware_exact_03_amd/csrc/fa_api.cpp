@@ -83,7 +83,8 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     const uint64_t lse_bytes = (uint64_t)B * H * N * sizeof(float);
     if (lse && overlaps(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
 
-    if (order != FA_ORDER_ASCENDING && order != FA_ORDER_DESCENDING) return FA_ERR_INVALID_ARG;
+    if (order != FA_ORDER_ASCENDING && order != FA_ORDER_DESCENDING && order != FA_ORDER_SHUFFLED)
+        return FA_ERR_INVALID_ARG;
     int tbr = 0, tbc = 0;
     const fa::Instance *inst = nullptr;
     bool study = false;

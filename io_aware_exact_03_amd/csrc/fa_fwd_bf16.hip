@@ -134,11 +134,40 @@ __global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf
         if (blk == blk0) return t;
         return blk < 0 ? -1 : min(ntiles - 1, blk * (128 / BC) + 128 / BC - 1);
     };
-    // Key tiles are visited in ascending order, or descending when asked
-    // (the tile-order axis of the deviation study).
-    const bool descending = a.order == 1;
-    auto first_tile = [&]() { return descending ? prev_tile(ntiles - 1) : next_tile(0); };
-    auto following = [&](int t) { return descending ? prev_tile(t - 1) : next_tile(t + 1); };
+    // Key tiles are visited in ascending order, or descending, or shuffled
+    // when asked (the tile-order axis of the deviation study).  The loop
+    // walks a cursor; tile_at maps it to a key tile.  Shuffled: cursor i is
+    // the i-th visit and goes to tile (sa * i + sb) mod ntiles, where sa is
+    // the smallest integer >= round(0.618 * ntiles) coprime to ntiles (so
+    // the map is a permutation) and sb = ntiles / 2; tiles the block mask
+    // turns off are passed over.
+    const bool descending = a.order == 1, shuffled = a.order == 2;
+    int sa = 1;
+    const int sb = ntiles / 2;
+    if (shuffled && ntiles > 1) {
+        sa = max(1, (ntiles * 618 + 500) / 1000);
+        for (;; ++sa) {
+            int x = sa, y = ntiles;
+            while (y) {
+                const int r = x % y;
+                x = y;
+                y = r;
+            }
+            if (x == 1) break;
+        }
+    }
+    auto tile_at = [&](int cur) { return shuffled ? (int)(((int64_t)sa * cur + sb) % ntiles) : cur; };
+    auto next_shuffled = [&](int cur) {
+        if (mrow)
+            while (cur < ntiles && mrow[(tile_at(cur) * BC) >> 7] == 0) ++cur;
+        return cur;
+    };
+    auto first_tile = [&]() {
+        return shuffled ? next_shuffled(0) : descending ? prev_tile(ntiles - 1) : next_tile(0);
+    };
+    auto following = [&](int t) {
+        return shuffled ? next_shuffled(t + 1) : descending ? prev_tile(t - 1) : next_tile(t + 1);
+    };
     auto valid = [&](int t) { return t >= 0 && t < ntiles; };
 
     // Q fragments (B operand of S^T = K Q^T), resident for the whole kernel.
@@ -277,20 +306,20 @@ __global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf
     // other buffer), start copying the next tile into the other buffer,
     // compute tile t.
     int t = first_tile();
-    if (valid(t)) copy_tile<C, D>(K, V, k_lds0, v_lds0, t * BC, klast, wave, lane);
+    if (valid(t)) copy_tile<C, D>(K, V, k_lds0, v_lds0, tile_at(t) * BC, klast, wave, lane);
     while (valid(t)) {
         int tn = following(t);
         wait_copies();
         __syncthreads();
-        if (valid(tn)) copy_tile<C, D>(K, V, k_lds1, v_lds1, tn * BC, klast, wave, lane);
-        compute(t, k_lds0, v_lds0);
+        if (valid(tn)) copy_tile<C, D>(K, V, k_lds1, v_lds1, tile_at(tn) * BC, klast, wave, lane);
+        compute(tile_at(t), k_lds0, v_lds0);
         t = tn;
         if (!valid(t)) break;
         tn = following(t);
         wait_copies();
         __syncthreads();
-        if (valid(tn)) copy_tile<C, D>(K, V, k_lds0, v_lds0, tn * BC, klast, wave, lane);
-        compute(t, k_lds1, v_lds1);
+        if (valid(tn)) copy_tile<C, D>(K, V, k_lds0, v_lds0, tile_at(tn) * BC, klast, wave, lane);
+        compute(tile_at(t), k_lds1, v_lds1);
         t = tn;
     }
 

@@ -20,7 +20,7 @@ struct FwdArgs {
     int Hkv;                    // key/value heads (H for plain multi-head attention)
     int group;                  // H / Hkv query heads per key/value head
     int nkb;                    // ceil(N/128): row length of block_mask
-    int order;                  // key-tile visit order: 0 ascending, 1 descending
+    int order;                  // key-tile visit order: 0 ascending, 1 descending, 2 shuffled
                                 // (tile-study kernels only)
     float scale_log2;           // softmax scale * log2(e), fp32
 };

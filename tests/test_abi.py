@@ -92,9 +92,11 @@ def test_gqa_invalid_arguments_return_status_without_launch(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(order=2), 7), (dict(order=-1), 7),
-    # descending order only on the tile-study kernels (bf16, d = 128, explicit tile)
+    (dict(order=3), 7), (dict(order=-1), 7),
+    # descending and shuffled orders only on the tile-study kernels (bf16, d = 128, explicit tile)
     (dict(order=1), 5), (dict(order=1, d=64, Br=128, Bc=64), 5),
+    (dict(order=2), 5), (dict(order=2, d=64, Br=64, Bc=64), 5), (dict(order=2, dtype=1, Br=64, Bc=64), 5),
+    (dict(order=2, d=128, Br=32, Bc=32, o=None), 1),
     (dict(order=1, dtype=1), 5), (dict(order=1, Br=256, Bc=64), 5), (dict(order=1, dtype=2, Br=128, Bc=64), 5),
     (dict(order=1, d=128, Br=64, Bc=32, q=None), 1),
 ])

@@ -398,10 +398,13 @@ def test_f16_long_causal_slice():
 # ---------------------------------------------------------------- tile order (deviation study)
 
 
+@pytest.mark.parametrize("order", ["descending", "shuffled"])
 @pytest.mark.parametrize("Br,Bc", [(16, 16), (64, 32), (128, 128)])
 @pytest.mark.parametrize("N", [300, 1000])
 @pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
-def test_descending_tile_order(Br, Bc, N, mode):
+def test_nonascending_tile_order(order, Br, Bc, N, mode):
+    # key-tile counts per workgroup span 1 .. 63, odd and even (the shuffled
+    # visit map must be a permutation of each count)
     inp = custom(2, 2, N, 128, seed=60 + N + Br, **modes_for(N, 61)[mode])
     q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
     kl = torch.from_numpy(inp["key_len"]).cuda() if inp.get("key_len") is not None else None
@@ -409,16 +412,20 @@ def test_descending_tile_order(Br, Bc, N, mode):
     out = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
     fa.fwd(q, k, v, causal=inp["causal"], key_len=kl, block_mask=bm, scale=float(inp["scale"]),
-           Br=Br, Bc=Bc, out=out, lse=lse, tile_order=fa.ORDER_DESCENDING)
+           Br=Br, Bc=Bc, out=out, lse=lse, tile_order=ORDERS[order])
     torch.cuda.synchronize()
     check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16,
-          f"descending Br={Br} Bc={Bc} N={N} {mode}")
+          f"{order} Br={Br} Bc={Bc} N={N} {mode}")
 
 
-def test_descending_tile_order_fully_masked_rows():
+ORDERS = {"descending": fa.ORDER_DESCENDING, "shuffled": fa.ORDER_SHUFFLED}
+
+
+@pytest.mark.parametrize("order", ["descending", "shuffled"])
+def test_nonascending_tile_order_fully_masked_rows(order):
     inp = custom(2, 2, 200, 128, seed=62, key_len=[0, 130])
     q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
     kl = torch.from_numpy(inp["key_len"]).cuda()
-    out, lse = fa.fwd(q, k, v, key_len=kl, Br=32, Bc=64, tile_order=fa.ORDER_DESCENDING)
+    out, lse = fa.fwd(q, k, v, key_len=kl, Br=32, Bc=64, tile_order=ORDERS[order])
     torch.cuda.synchronize()
-    check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16, "desc masked")
+    check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16, f"{order} masked")

@@ -9,8 +9,8 @@ The slice is rows 0..2047 of heads 0..3 of the 16K causal workload's tensors
 self-contained problem.  The precision rows feed the same float32 draw
 rounded to fp16, or unrounded to the fp32 path.
 
-It also runs a few tiles with the key tiles visited last-first (the
-tile-order axis of the same study).  For every (Br, Bc) it prints max|dO|, mean|dO|, max|dLSE| against the oracle
+It also runs a few tiles with the key tiles visited last-first and in a
+fixed shuffled order (the tile-order axis of the same study).  For every (Br, Bc) it prints max|dO|, mean|dO|, max|dLSE| against the oracle
 and the kernel time per launch (HIP events on the launch stream).  The trend
 is reported, not asserted; the per-point bar (max|dO| <= 2e-2) is asserted by
 the GPU parity tests.
@@ -33,8 +33,10 @@ import oracle  # noqa: E402
 from workloads import WORKLOADS, causal_prefix  # noqa: E402
 
 PAIRS = [(br, bc) for br in (16, 32, 64, 128) for bc in (16, 32, 64, 128)] + [(256, 64), (0, 0)]
-# the tile-order axis: descending key-tile order on the tile-study kernels
+# the tile-order axis: descending and shuffled key-tile orders on the
+# tile-study kernels
 DESC = [(16, 16), (32, 64), (64, 64), (128, 16), (128, 64), (128, 128)]
+ORDER_NAME = {0: "asc", 1: "desc", 2: "shuffled"}
 
 
 def main():
@@ -51,7 +53,8 @@ def main():
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     pairs = 4 * 2048 * 2049 // 2
     rows = []
-    for br, bc, order in [(br, bc, 0) for br, bc in PAIRS] + [(br, bc, 1) for br, bc in DESC]:
+    for br, bc, order in ([(br, bc, 0) for br, bc in PAIRS] + [(br, bc, 1) for br, bc in DESC]
+                          + [(br, bc, 2) for br, bc in DESC]):
         def call():
             fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, out=out, lse=lse,
                    tile_order=order)
@@ -72,7 +75,7 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.reps
         tb, tc = fa.fa_tile_shape(0, 128, False, br, bc)
-        rows.append(dict(Br=tb, Bc=tc, default=(br, bc) == (0, 0), order="desc" if order else "asc",
+        rows.append(dict(Br=tb, Bc=tc, default=(br, bc) == (0, 0), order=ORDER_NAME[order],
                          max_dO=float(d_o.max()),
                          mean_dO=float(d_o.mean()), max_dLSE=float(d_l.max()), us=us,
                          tflops=4 * 128 * pairs / (us * 1e-6) / 1e12))
