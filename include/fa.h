@@ -1,7 +1,8 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (forward,
+ * and the backward pass of the bf16 forward).
  *
- * The library computes, for every batch entry b and head h,
+ * The forward entry points compute, for every batch entry b and head h,
  *
  *     S   = scale * Q K^T                      (N x N, never stored)
  *     A   = row-softmax(S), disallowed keys at -inf before the softmax

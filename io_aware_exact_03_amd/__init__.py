@@ -1,12 +1,12 @@
-"""Python binding of the gfx950 exact-attention forward library (libfa.so).
+"""Python binding of the gfx950 exact-attention library (libfa.so).
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
 ``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_tile_shape``,
 ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
-the library's HIP kernels.  ``fwd`` is a convenience wrapper that allocates
-the outputs with torch and passes torch's current stream.  There is no
+the library's HIP kernels.  ``fwd`` and ``bwd`` are convenience wrappers
+that allocate the outputs with torch and pass torch's current stream.  There is no
 fallback: if libfa.so is missing or fails to load, every call raises.
 """
 import ctypes

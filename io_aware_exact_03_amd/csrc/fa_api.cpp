@@ -1,4 +1,4 @@
-// C ABI of the attention forward library: argument validation (before any
+// C ABI of the attention library (forward and backward): argument validation (before any
 // HIP call), tile selection and kernel launch.  Semantics are documented in
 // include/fa.h.
 #include "fa.h"
