@@ -53,6 +53,16 @@ def _configure(lib):
                                          ctypes.c_double, ctypes.c_int,
                                          ctypes.c_void_p, ctypes.c_void_p, i64]
     lib.attn_bwd_ref_gqa_f64.restype = ctypes.c_int
+    lib.attn_bwd_rows_gqa_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                          ctypes.c_double, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p, i64,
+                                          ctypes.c_void_p, i64, dp]
+    lib.attn_bwd_rows_gqa_f64.restype = ctypes.c_int
+    lib.attn_bwd_cols_gqa_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                          ctypes.c_double, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p, i64,
+                                          ctypes.c_void_p, i64, dp, dp]
+    lib.attn_bwd_cols_gqa_f64.restype = ctypes.c_int
     lib.attn_ref_threads.restype = ctypes.c_int
     return lib
 
@@ -163,9 +173,54 @@ def attention_bwd_f64(q, k, v, dout, scale, causal=False, key_len=None, block_ma
     return dq, dk, dv
 
 
+def attention_bwd_rows_f64(q, k, v, dout, rows, scale, causal=False, key_len=None,
+                           block_mask=None, block=128):
+    """dQ (float64, [n, d]) for selected query rows only; ``rows`` holds flat
+    row indices (b*H + h)*N + i.  Same definition as attention_bwd_f64."""
+    q, k, v, kl, bm = _prep(q, k, v, key_len, block_mask, block)
+    dout = _f64(dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    B, H, N, d = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    dq = np.empty((rows.size, d), dtype=np.float64)
+    rc = _load().attn_bwd_rows_gqa_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, k.shape[1], N, d, float(scale),
+        int(bool(causal)), kl.ctypes.data if kl is not None else None,
+        bm.ctypes.data if bm is not None else None, block, rows.ctypes.data, rows.size, _ptr(dq))
+    if rc != 0:
+        raise RuntimeError(f"attn_bwd_rows_gqa_f64 failed with code {rc}")
+    return dq
+
+
+def attention_bwd_cols_f64(q, k, v, dout, cols, scale, causal=False, key_len=None,
+                           block_mask=None, block=128):
+    """(dK, dV) (float64, [n, d] each) for selected keys only; ``cols`` holds
+    flat key indices (b*H_kv + g)*N + j.  Same definition as
+    attention_bwd_f64; costs one forward pass of the query heads that read
+    the key/value heads involved."""
+    q, k, v, kl, bm = _prep(q, k, v, key_len, block_mask, block)
+    dout = _f64(dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    B, H, N, d = q.shape
+    cols = np.ascontiguousarray(cols, dtype=np.int64).reshape(-1)
+    dk = np.empty((cols.size, d), dtype=np.float64)
+    dv = np.empty((cols.size, d), dtype=np.float64)
+    rc = _load().attn_bwd_cols_gqa_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, k.shape[1], N, d, float(scale),
+        int(bool(causal)), kl.ctypes.data if kl is not None else None,
+        bm.ctypes.data if bm is not None else None, block, cols.ctypes.data, cols.size,
+        _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise RuntimeError(f"attn_bwd_cols_gqa_f64 failed with code {rc}")
+    return dk, dv
+
+
 def threads():
     """OpenMP threads the oracle's parallel regions use."""
     return int(_load().attn_ref_threads())
 
 
-__all__ = ["attention_f64", "attention_rows_f64", "attention_bwd_f64", "threads"]
+__all__ = ["attention_f64", "attention_rows_f64", "attention_bwd_f64", "attention_bwd_rows_f64",
+           "attention_bwd_cols_f64", "threads"]

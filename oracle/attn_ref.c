@@ -310,6 +310,147 @@ int attn_bwd_ref_gqa_f64(const double *q, const double *k, const double *v,
     return 0;
 }
 
+/* Sampled gradients, by row: dQ_i for the query rows listed in rows[]
+ * (flat index (b * H + h) * N + i), each from that row of A evaluated on its
+ * own -- the same formulas as the full backward above, restricted to one
+ * row:  D_i = dO_i . O_i,  dQ_i = scale * sum_j A_ij (dO_i . V_j - D_i) K_j.
+ * dq_rows is [n_rows, d]. */
+int attn_bwd_rows_gqa_f64(const double *q, const double *k, const double *v,
+                          const double *dout, int64_t B, int64_t H, int64_t Hkv,
+                          int64_t N, int64_t d, double scale, int causal,
+                          const int32_t *key_len, const uint8_t *block_mask,
+                          int64_t blk, const int64_t *rows, int64_t n_rows,
+                          double *dq_rows)
+{
+    int rc = check_args(q, k, v, B, H, Hkv, N, d, block_mask, blk);
+    if (rc) return rc;
+    if (!dout || (n_rows > 0 && (!rows || !dq_rows))) return 1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * H * N) return 2;
+    if (n_rows == 0) return 0;
+    const int64_t nkb = block_mask ? (N + blk - 1) / blk : 0;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        double *o = (double *)malloc((size_t)d * sizeof(double));
+        if (!s || !o) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (!s || !o) continue;
+            const int64_t flat = rows[r];
+            const int64_t head = flat / N, i = flat % N, b = head / H;
+            const int64_t kvh = kv_head(b, head - b * H, H, Hkv);
+            const double *kh = k + kvh * N * d, *vh = v + kvh * N * d;
+            const double *doi = dout + flat * d;
+            double lse_unused;
+            score_row(s, q + flat * d, kh, i, b, N, d, scale, causal, key_len,
+                      block_mask, blk, nkb);
+            softmax_row_times_v(s, vh, o, &lse_unused, N, d);
+            double Di = 0.0;
+            for (int64_t c = 0; c < d; ++c) Di += doi[c] * o[c];
+            double *dqi = dq_rows + r * d;
+            for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                const double a = s[j];
+                if (a == 0.0) continue;
+                double da = 0.0;
+                for (int64_t c = 0; c < d; ++c) da += doi[c] * vh[j * d + c];
+                const double ds = a * (da - Di);
+                for (int64_t c = 0; c < d; ++c) dqi[c] += scale * ds * kh[j * d + c];
+            }
+        }
+        free(s);
+        free(o);
+    }
+    return failed ? 3 : 0;
+}
+
+/* Sampled gradients, by key: dK_j and dV_j for the keys listed in cols[]
+ * (flat index (b * Hkv + g) * N + j), summed over every query row of every
+ * query head that reads key/value head g:
+ *     dV_j = sum_i A_ij dO_i,   dK_j = scale * sum_i A_ij (dO_i . V_j - D_i) Q_i.
+ * Each query row's A row, O_i and D_i are evaluated on their own, so the
+ * cost is one forward pass of the query heads involved.  dk_cols and
+ * dv_cols are [n_cols, d]. */
+int attn_bwd_cols_gqa_f64(const double *q, const double *k, const double *v,
+                          const double *dout, int64_t B, int64_t H, int64_t Hkv,
+                          int64_t N, int64_t d, double scale, int causal,
+                          const int32_t *key_len, const uint8_t *block_mask,
+                          int64_t blk, const int64_t *cols, int64_t n_cols,
+                          double *dk_cols, double *dv_cols)
+{
+    int rc = check_args(q, k, v, B, H, Hkv, N, d, block_mask, blk);
+    if (rc) return rc;
+    if (!dout || (n_cols > 0 && (!cols || !dk_cols || !dv_cols))) return 1;
+    for (int64_t r = 0; r < n_cols; ++r)
+        if (cols[r] < 0 || cols[r] >= B * Hkv * N) return 2;
+    for (int64_t x = 0; x < n_cols * d; ++x) dk_cols[x] = dv_cols[x] = 0.0;
+    if (n_cols == 0) return 0;
+    const int64_t nkb = block_mask ? (N + blk - 1) / blk : 0, G = H / Hkv;
+    int failed = 0;
+    for (int64_t x = 0; x < B * Hkv; ++x) {
+        int64_t any = 0;
+        for (int64_t r = 0; r < n_cols; ++r) any |= cols[r] / N == x;
+        if (!any) continue;
+        const int64_t b = x / Hkv, g = x % Hkv;
+        const double *kh = k + x * N * d, *vh = v + x * N * d;
+        for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+            const int64_t head = (b * H + h) * N;
+            const double *qh = q + head * d, *doh = dout + head * d;
+#pragma omp parallel
+            {
+                double *s = (double *)malloc((size_t)N * sizeof(double));
+                double *o = (double *)malloc((size_t)d * sizeof(double));
+                double *acc = (double *)calloc((size_t)(2 * n_cols * d), sizeof(double));
+                if (!s || !o || !acc) {
+#pragma omp atomic write
+                    failed = 1;
+                }
+#pragma omp for schedule(dynamic, 16)
+                for (int64_t i = 0; i < N; ++i) {
+                    if (!s || !o || !acc) continue;
+                    double lse_unused;
+                    score_row(s, qh + i * d, kh, i, b, N, d, scale, causal, key_len,
+                              block_mask, blk, nkb);
+                    softmax_row_times_v(s, vh, o, &lse_unused, N, d);
+                    const double *doi = doh + i * d, *qi = qh + i * d;
+                    double Di = 0.0;
+                    for (int64_t c = 0; c < d; ++c) Di += doi[c] * o[c];
+                    for (int64_t r = 0; r < n_cols; ++r) {
+                        if (cols[r] / N != x) continue;
+                        const int64_t j = cols[r] % N;
+                        const double a = s[j];
+                        if (a == 0.0) continue;
+                        double da = 0.0;
+                        for (int64_t c = 0; c < d; ++c) da += doi[c] * vh[j * d + c];
+                        const double ds = a * (da - Di);
+                        double *ak = acc + r * d, *av = acc + (n_cols + r) * d;
+                        for (int64_t c = 0; c < d; ++c) {
+                            av[c] += a * doi[c];
+                            ak[c] += scale * ds * qi[c];
+                        }
+                    }
+                }
+                if (acc) {
+#pragma omp critical
+                    for (int64_t y = 0; y < n_cols * d; ++y) {
+                        dk_cols[y] += acc[y];
+                        dv_cols[y] += acc[n_cols * d + y];
+                    }
+                }
+                free(s);
+                free(o);
+                free(acc);
+            }
+        }
+    }
+    return failed ? 3 : 0;
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int attn_ref_threads(void)
 {

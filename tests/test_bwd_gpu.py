@@ -17,7 +17,7 @@ torch = pytest.importorskip("torch")
 
 import io_aware_exact_03_amd as fa  # noqa: E402
 import oracle  # noqa: E402
-from workloads import random_qkv, band_global_block_mask  # noqa: E402
+from workloads import WORKLOADS, make_inputs, random_qkv, band_global_block_mask  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -85,10 +85,52 @@ def test_bwd_modes(d, N, mode):
     run_case(2, 2, 2, N, d, seed=70 + N + d, **modes(N, 71)[mode])
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("H,H_kv", [(8, 2), (4, 1)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_grouped_heads(H, H_kv, causal):
-    run_case(1, H, H_kv, 200, 128, seed=72, causal=causal)
+def test_bwd_grouped_heads(d, H, H_kv, causal):
+    run_case(1, H, H_kv, 200, d, seed=72, causal=causal)
+
+
+@pytest.mark.parametrize("mode", ["padded", "blocks", "all"])
+def test_bwd_grouped_heads_masked(mode):
+    run_case(2, 6, 2, 300, 64, seed=77, **modes(300, 78)[mode])
+
+
+@pytest.mark.parametrize("workload", ["gpt2_causal", "bert_padded", "long_causal", "block_sparse"])
+def test_bwd_full_size_sampled(workload):
+    # The whole workload at its full size, in the launch configuration the
+    # backward report times; dQ checked on sampled query rows, dK and dV on
+    # sampled keys of one key/value head, each against the FP64 oracle
+    # evaluated for just those outputs.
+    w = WORKLOADS[workload]
+    inp = make_inputs(w)
+    rng = np.random.default_rng(w.seed + 500)
+    tq, tk, tv = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    tdo = dev(rng.standard_normal(inp["q"].shape, dtype=np.float32))
+    kl = torch.from_numpy(inp["key_len"]).cuda() if inp["key_len"] is not None else None
+    bm = torch.from_numpy(inp["block_mask"]).cuda() if inp["block_mask"] is not None else None
+    scale = float(inp["scale"])
+    o, lse = fa.fwd(tq, tk, tv, causal=w.causal, key_len=kl, block_mask=bm, scale=scale)
+    dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, key_len=kl, block_mask=bm, scale=scale)
+    torch.cuda.synchronize()
+    B, H, N, d = inp["q"].shape
+    rows = rng.choice(B * H * N, size=24, replace=False)
+    x = int(rng.integers(B * H))  # one key/value head (H_kv = H here)
+    keys = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=10, replace=False)]))
+    cols = x * N + keys
+    args = (scale, w.causal, inp["key_len"], inp["block_mask"])
+    dout = tdo.float().cpu().numpy()
+    ref_dq = oracle.attention_bwd_rows_f64(inp["q"], inp["k"], inp["v"], dout, rows, *args)
+    ref_dk, ref_dv = oracle.attention_bwd_cols_f64(inp["q"], inp["k"], inp["v"], dout, cols, *args)
+    rows_t, cols_t = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    got = {"dq": dq.reshape(-1, d)[rows_t], "dk": dk.reshape(-1, d)[cols_t], "dv": dv.reshape(-1, d)[cols_t]}
+    for name, r in (("dq", ref_dq), ("dk", ref_dk), ("dv", ref_dv)):
+        g = got[name].double().cpu().numpy()
+        assert np.all(np.isfinite(g)), f"{workload} {name}: non-finite"
+        err = float(np.abs(g - r).max())
+        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        assert err <= bound, f"{workload} {name}: max|dg| = {err:.3e} > {bound:.3e}"
 
 
 def test_bwd_larger_causal():

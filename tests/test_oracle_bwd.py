@@ -117,3 +117,47 @@ def test_fully_masked_batch_has_no_gradient():
     for g in (dq, dk, dv):
         assert not np.any(g[1])
         assert np.any(g[0])
+
+
+def _masks(N, block, B, rng):
+    nb = (N + block - 1) // block
+    return {
+        "dense": dict(causal=False, key_len=None, bm=None),
+        "causal": dict(causal=True, key_len=None, bm=None),
+        "padded": dict(causal=False, key_len=np.array([N - 9, N, 3][:B], dtype=np.int32), bm=None),
+        "blocks": dict(causal=False, key_len=None, bm=(rng.random(nb * nb) < 0.5).astype(np.uint8)),
+        "all": dict(causal=True, key_len=np.array([N, 0, N - 4][:B], dtype=np.int32),
+                    bm=(rng.random(nb * nb) < 0.6).astype(np.uint8)),
+    }
+
+
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (4, 2), (3, 1)])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_sampled_gradients_match_full_backward(H, H_kv, mode):
+    # The sampled-row dQ and sampled-key dK/dV evaluations (used to check the
+    # GPU backward at full workload sizes) against the full backward, which
+    # is pinned by finite differences above.
+    B, N, d, block, scale = 3, 37, 16, 8, 0.3
+    q, _, _, rng = random_qkv(B, H, N, d, seed=900 + H, dtype="f32")
+    _, k, v, rng = random_qkv(B, H_kv, N, d, seed=910 + H, dtype="f32", rng=rng)
+    dout = rng.standard_normal(q.shape)
+    m = _masks(N, block, B, rng)[mode]
+    args = (m["causal"], m["key_len"], m["bm"], block)
+    dq, dk, dv = oracle.attention_bwd_f64(q, k, v, dout, scale, *args)
+    rows = rng.choice(B * H * N, size=25, replace=False)
+    cols = np.concatenate([rng.choice(B * H_kv * N, size=15, replace=False), [0, B * H_kv * N - 1, 0]])
+    dq_r = oracle.attention_bwd_rows_f64(q, k, v, dout, rows, scale, *args)
+    dk_c, dv_c = oracle.attention_bwd_cols_f64(q, k, v, dout, cols, scale, *args)
+    np.testing.assert_allclose(dq_r, dq.reshape(-1, d)[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk_c, dk.reshape(-1, d)[cols], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv_c, dv.reshape(-1, d)[cols], rtol=0, atol=1e-12)
+
+
+def test_sampled_gradients_reject_bad_indices():
+    q, k, v, rng = random_qkv(1, 2, 10, 4, seed=920, dtype="f32")
+    dout = rng.standard_normal(q.shape)
+    with pytest.raises(RuntimeError):
+        oracle.attention_bwd_rows_f64(q, k, v, dout, [20], 0.5)
+    with pytest.raises(RuntimeError):
+        oracle.attention_bwd_cols_f64(q, k, v, dout, [-1], 0.5)
+    assert oracle.attention_bwd_rows_f64(q, k, v, dout, [], 0.5).shape == (0, 4)
