@@ -12,7 +12,7 @@
 // P = exp(S - LSE), dP = dO V^T, Delta_i = dO_i . O_i, dS = P * (dP - Delta):
 //     dV = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K.
 //
-// Three kernels:
+// Kernels:
 //  * bwd_delta: Delta_i = dO_i . O_i per query row (fp32, caller workspace).
 //  * bwd_dkdv: one workgroup per block of 32*NW keys of one key/value head;
 //    each wave keeps its 32 keys' K and V fragments and the dK^T, dV^T
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 // ---------------------------------------------------------------- dK, dV
 
 template <int D, int NW, int QT, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv(BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     using Geo = BwdGeom<D>;
     constexpr int NQK = Geo::NQK, ND = Geo::ND, BK = 32 * NW, BQ = 32 * QT;
     static_assert(128 % BQ == 0, "a query tile lies inside one 128-row mask block");
@@ -701,9 +701,9 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
-    // query rows per step: 128 for d = 128 (512-register mode), 64 for d = 64
-    // (two workgroups per CU; 128 rows would spill)
-    constexpr int QT = D == 128 ? 4 : 2;
+    // bwd_dkdv (d = 64 without the causal mask): 64 query rows per step, two
+    // workgroups per CU (128 rows would spill)
+    constexpr int QT = 2;
     if constexpr (D == 128 || CAUSAL)
         hipLaunchKernelGGL((bwd_dkdv_pair<D, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0, stream,
                            a);
