@@ -239,7 +239,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     for (int mb = 0; mb < ND; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
-    float m = kNegInf, l = 0.f;
+    // m starts at the most negative finite float rather than -inf, so that
+    // m - m_new and s*c - m never meet inf - inf: masked scores (-inf) still
+    // give p = 0, a tile with no allowed key leaves m unchanged (alpha = 1),
+    // and the first allowed key makes alpha = exp2(-huge) = 0 while O and l
+    // are still 0.  Rows that never see a key keep l = 0 (LSE = -inf, O = 0).
+    float m = -__FLT_MAX__, l = 0.f;
     // Scores ping-pong between sA and sB across consecutive iterations.
     acc_t sA[NKB], sB[NKB];
 
@@ -315,12 +320,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
                 for (int j = 0; j < 8; ++j) mx = fmaxf(mx, s[kb][i0 + j]);
                 pin(mx);
             } else if constexpr (kind == kChunkRed) {
-                mx = group_max<32>(mx);
-                const float m_tile = mx == kNegInf ? kNegInf : mx * c;
-                const float m_new = fmaxf(m, m_tile);
-                const float m_use = m_new == kNegInf ? 0.f : m_new;
-                alpha = fast_exp2(m - m_use);
-                neg_m = -m_use;
+                // Row max over the partner lane (permlane32 swap), scaled
+                // by c > 0 before the max: one three-way max, no -inf guards.
+                const auto r = __builtin_amdgcn_permlane32_swap(f2u(mx), f2u(mx), false, false);
+                const float m_new = fmaxf(fmaxf(m, u2f(r[0]) * c), u2f(r[1]) * c);
+                alpha = fast_exp2(m - m_new);
+                neg_m = -m_new;
                 m = m_new;
                 // O needs rescaling only when some row's maximum moved
                 // (alpha = 1 exactly otherwise).
