@@ -113,11 +113,11 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
  *           FA_DTYPE_F32 (float)
  *   Br    : query rows per tile;  Bc : key rows per tile.
  * Br = Bc = 0 selects the tuned default (what fa_fwd / fa_fwd_f32 use).  For
- * bf16 every Br, Bc in {16, 32, 64, 128} is built for d = 128 (one
- * tile-study kernel family), and the tuned shapes (Br, Bc) = (128, 64) and
- * (256, 64) for d = 64 and 128; (256, 64) does not take a block mask.  fp16
- * builds (128, 64) for d = 64 and 128, fp32 only its default.  Unbuilt pairs
- * return FA_ERR_UNSUPPORTED_TILE.
+ * bf16 every Br, Bc in {16, 32, 64, 128} is built for d = 64 and 128 (the
+ * tile-study kernel family; an explicit (128, 64) runs it, not the tuned
+ * kernel that the default (128, 64) runs), plus the tuned (256, 64), which
+ * does not take a block mask.  fp16 builds (128, 64) for d = 64 and 128,
+ * fp32 only its default.  Unbuilt pairs return FA_ERR_UNSUPPORTED_TILE.
  */
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N, int d, float scale, int causal,
@@ -141,7 +141,7 @@ enum { FA_ORDER_ASCENDING = 0, FA_ORDER_DESCENDING = 1, FA_ORDER_SHUFFLED = 2 };
  *                Other values: FA_ERR_INVALID_ARG.
  * The result is the same attention up to rounding; only the order of the
  * running-maximum/rescale steps changes.  Orders other than ascending run
- * on the tile-study kernels only (bf16, d = 128, explicit Br, Bc in
+ * on the tile-study kernels only (bf16, d = 64 or 128, explicit Br, Bc in
  * {16, 32, 64, 128}); other tiles return FA_ERR_UNSUPPORTED_TILE.
  */
 int fa_fwd_study(const void *q, const void *k, const void *v, void *o, float *lse,

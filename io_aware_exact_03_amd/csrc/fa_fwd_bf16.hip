@@ -380,12 +380,16 @@ struct Pick {
 }  // namespace
 
 const Instance *bf16_instances() {
-    // Tile-size study: every (Br, Bc) in {16, 32, 64, 128}^2 for d = 128.
+    // Tile-size study: every (Br, Bc) in {16, 32, 64, 128}^2 for d = 64 and 128.
     static const Instance table[] = {
         FA_BF16_ROW(128, 16),
         FA_BF16_ROW(128, 32),
         FA_BF16_ROW(128, 64),
         FA_BF16_ROW(128, 128),
+        FA_BF16_ROW(64, 16),
+        FA_BF16_ROW(64, 32),
+        FA_BF16_ROW(64, 64),
+        FA_BF16_ROW(64, 128),
         Instance{0, 0, 0, 0, nullptr},
     };
     return table;

@@ -60,7 +60,7 @@ def call(**kw):
     (dict(q=Q + 8), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4), (dict(key_len=0x60000002), 4),
     (dict(Br=48, Bc=64), 5), (dict(Br=128, Bc=256), 5), (dict(dtype=3), 5), (dict(dtype=-1), 5),
     (dict(dtype=2, Br=64, Bc=32), 5),
-    (dict(dtype=1, Br=16, Bc=16), 5), (dict(d=64, Br=16, Bc=16), 5),
+    (dict(dtype=1, Br=16, Bc=16), 5), (dict(d=64, Br=16, Bc=256), 5),
     (dict(Br=256, Bc=64, block_mask=0x70000000), 5),
     (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
     (dict(o=Q + 64), 7), (dict(lse=O + 16), 7), (dict(lse=O - 2 * 3 * 100 * 4 + 4), 7),
@@ -94,8 +94,8 @@ def test_gqa_invalid_arguments_return_status_without_launch(kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(order=3), 7), (dict(order=-1), 7),
     # descending and shuffled orders only on the tile-study kernels (bf16, d = 128, explicit tile)
-    (dict(order=1), 5), (dict(order=1, d=64, Br=128, Bc=64), 5),
-    (dict(order=2), 5), (dict(order=2, d=64, Br=64, Bc=64), 5), (dict(order=2, dtype=1, Br=64, Bc=64), 5),
+    (dict(order=1), 5), (dict(order=1, d=64, Br=256, Bc=64), 5),
+    (dict(order=2), 5), (dict(order=2, d=64), 5), (dict(order=2, dtype=1, Br=64, Bc=64), 5),
     (dict(order=2, d=128, Br=32, Bc=32, o=None), 1),
     (dict(order=1, dtype=1), 5), (dict(order=1, Br=256, Bc=64), 5), (dict(order=1, dtype=2, Br=128, Bc=64), 5),
     (dict(order=1, d=128, Br=64, Bc=32, q=None), 1),
@@ -164,9 +164,10 @@ def test_tile_table():
         # a block mask needs a tile no taller than one 128-token mask block
         br, bc = fa.fa_tile_shape(fa.DTYPE_BF16, d, block_sparse=True)
         assert br <= 128
-    for br in (16, 32, 64, 128):
-        for bc in (16, 32, 64, 128):
-            assert fa.fa_tile_shape(fa.DTYPE_BF16, 128, False, br, bc) == (br, bc)
+    for d in (64, 128):
+        for br in (16, 32, 64, 128):
+            for bc in (16, 32, 64, 128):
+                assert fa.fa_tile_shape(fa.DTYPE_BF16, d, False, br, bc) == (br, bc)
     assert fa.fa_tile_shape(fa.DTYPE_BF16, 64, False, 128, 64) == (128, 64)
     assert fa.fa_tile_shape(fa.DTYPE_BF16, 128, False, 256, 64) == (256, 64)
     assert fa.fa_tile_shape(fa.DTYPE_F32, 64) == (128, 32)
@@ -177,4 +178,4 @@ def test_tile_table():
     with pytest.raises(fa.FaError):
         fa.fa_tile_shape(fa.DTYPE_BF16, 128, True, 256, 64)
     with pytest.raises(fa.FaError):
-        fa.fa_tile_shape(fa.DTYPE_BF16, 64, False, 16, 16)
+        fa.fa_tile_shape(fa.DTYPE_BF16, 64, False, 16, 256)

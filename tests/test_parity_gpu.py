@@ -204,6 +204,17 @@ def test_tile_sweep_slice(Br, Bc):
     check(o, lse, *_PREFIX["ref"], TOL_BF16, f"sweep Br={Br} Bc={Bc}")
 
 
+@pytest.mark.parametrize("Br", [16, 32, 64, 128])
+@pytest.mark.parametrize("Bc", [16, 32, 64, 128])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_tile_study_d64(Br, Bc, mode):
+    """The tile-study kernels at d = 64: every (Br, Bc) on a ragged length
+    (300 = two full 128-row blocks and a 44-row tail) under every mask."""
+    inp = custom(2, 3, 300, 64, seed=80 + Br + Bc, **modes_for(300, 81)[mode])
+    o, lse = run(inp, Br=Br, Bc=Bc)
+    check(o, lse, *ref(inp), TOL_BF16, f"d=64 Br={Br} Bc={Bc} {mode}")
+
+
 # ---------------------------------------------------------------- closed forms on the GPU
 
 
@@ -400,12 +411,12 @@ def test_f16_long_causal_slice():
 
 @pytest.mark.parametrize("order", ["descending", "shuffled"])
 @pytest.mark.parametrize("Br,Bc", [(16, 16), (64, 32), (128, 128)])
-@pytest.mark.parametrize("N", [300, 1000])
+@pytest.mark.parametrize("N,d", [(300, 128), (1000, 128), (300, 64)])
 @pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
-def test_nonascending_tile_order(order, Br, Bc, N, mode):
+def test_nonascending_tile_order(order, Br, Bc, N, d, mode):
     # key-tile counts per workgroup span 1 .. 63, odd and even (the shuffled
     # visit map must be a permutation of each count)
-    inp = custom(2, 2, N, 128, seed=60 + N + Br, **modes_for(N, 61)[mode])
+    inp = custom(2, 2, N, d, seed=60 + N + Br, **modes_for(N, 61)[mode])
     q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
     kl = torch.from_numpy(inp["key_len"]).cuda() if inp.get("key_len") is not None else None
     bm = torch.from_numpy(inp["block_mask"]).cuda() if inp.get("block_mask") is not None else None
@@ -415,7 +426,7 @@ def test_nonascending_tile_order(order, Br, Bc, N, mode):
            Br=Br, Bc=Bc, out=out, lse=lse, tile_order=ORDERS[order])
     torch.cuda.synchronize()
     check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16,
-          f"{order} Br={Br} Bc={Bc} N={N} {mode}")
+          f"{order} Br={Br} Bc={Bc} N={N} d={d} {mode}")
 
 
 ORDERS = {"descending": fa.ORDER_DESCENDING, "shuffled": fa.ORDER_SHUFFLED}

@@ -1,13 +1,15 @@
-"""Tile-size deviation study on the causal 16K-token workload's prefix slice.
+"""Tile-size deviation study on causal prefix slices of two workloads.
 
 Block sizes Br (query rows per tile) and Bc (key rows per tile) are varied
 and each output is compared with the FP64 golden value, as in the
 micro-benchmark of the page "Is Flash Attention Stable?" (aibr.jp, sections 3
 and 4, where deviation falls as tiles grow because fewer rescalings happen).
-The slice is rows 0..2047 of heads 0..3 of the 16K causal workload's tensors
-(B=1, H=4, N=2048, d=128, inputs 0.5*N(0,1)): under the causal mask it is a
-self-contained problem.  The precision rows feed the same float32 draw
-rounded to fp16, or unrounded to the fp32 path.
+The slices are rows 0..2047 of heads 0..3 of the 16K causal workload's
+tensors (B=1, H=4, N=2048, d=128, inputs 0.5*N(0,1)) and rows 0..1023 of
+heads 0..3 of the GPT-2-sized causal workload (B=8, H=4, N=1024, d=64,
+N(0,1)): under the causal mask each is a self-contained problem.  The
+precision rows feed the same float32 draw rounded to fp16, or unrounded to
+the fp32 path.
 
 It also runs a few tiles with the key tiles visited last-first and in a
 fixed shuffled order (the tile-order axis of the same study).  For every (Br, Bc) it prints max|dO|, mean|dO|, max|dLSE| against the oracle
@@ -39,50 +41,54 @@ DESC = [(16, 16), (32, 64), (64, 64), (128, 16), (128, 64), (128, 128)]
 ORDER_NAME = {0: "asc", 1: "desc", 2: "shuffled"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--json", default=None)
-    ap.add_argument("--reps", type=int, default=20)
-    args = ap.parse_args()
-    w = WORKLOADS["long_causal"]
-    inp = causal_prefix(w, N=2048, H=4)
+SLICES = [
+    # (workload, rows N, heads H): a causal prefix is a self-contained problem
+    ("long_causal", 2048, 4),   # B=1 H=4 N=2048 d=128, 0.5*N(0,1)
+    ("gpt2_causal", 1024, 4),   # B=8 H=4 N=1024 d=64, N(0,1)
+]
+
+
+def sweep(key, N, H, reps, with_orders):
+    w = WORKLOADS[key]
+    inp = causal_prefix(w, N=N, H=H)
     scale = float(np.float32(inp["scale"]))
     o_ref, lse_ref = oracle.attention_f64(inp["q"], inp["k"], inp["v"], scale, True, None, None, 128)
     q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v"))
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    pairs = 4 * 2048 * 2049 // 2
+    B = q.shape[0]
+    pairs = B * H * N * (N + 1) // 2
     rows = []
-    for br, bc, order in ([(br, bc, 0) for br, bc in PAIRS] + [(br, bc, 1) for br, bc in DESC]
-                          + [(br, bc, 2) for br, bc in DESC]):
+    runs = [(br, bc, 0) for br, bc in PAIRS]
+    if with_orders:
+        runs += [(br, bc, 1) for br, bc in DESC] + [(br, bc, 2) for br, bc in DESC]
+    for br, bc, order in runs:
+
         def call():
             fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, out=out, lse=lse,
                    tile_order=order)
         call()
         torch.cuda.synchronize()
-        o = out.double().cpu().numpy()
-        l = lse.double().cpu().numpy()
-        d_o = np.abs(o - o_ref)
-        d_l = np.abs(l - lse_ref)
+        d_o = np.abs(out.double().cpu().numpy() - o_ref)
+        d_l = np.abs(lse.double().cpu().numpy() - lse_ref)
         s = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(3):
             call()
         e0.record(s)
-        for _ in range(args.reps):
+        for _ in range(reps):
             call()
         e1.record(s)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / args.reps
-        tb, tc = fa.fa_tile_shape(0, 128, False, br, bc)
-        rows.append(dict(Br=tb, Bc=tc, default=(br, bc) == (0, 0), order=ORDER_NAME[order],
-                         max_dO=float(d_o.max()),
-                         mean_dO=float(d_o.mean()), max_dLSE=float(d_l.max()), us=us,
-                         tflops=4 * 128 * pairs / (us * 1e-6) / 1e12))
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tb, tc = fa.fa_tile_shape(0, w.d, False, br, bc)
+        rows.append(dict(slice=key, d=w.d, Br=tb, Bc=tc, default=(br, bc) == (0, 0),
+                         order=ORDER_NAME[order], max_dO=float(d_o.max()), mean_dO=float(d_o.mean()),
+                         max_dLSE=float(d_l.max()), us=us, tflops=4 * w.d * pairs / (us * 1e-6) / 1e12))
     # Precision axis: the same float32 draw rounded to each I/O format, each
     # compared with the FP64 oracle on exactly the values it received.
     for fmt, tdt in (("f16", torch.float16), ("f32", torch.float32)):
-        x = causal_prefix(w, N=2048, H=4, fmt=fmt)
+        x = causal_prefix(w, N=N, H=H, fmt=fmt)
         o_r, l_r = oracle.attention_f64(x["q"], x["k"], x["v"], scale, True, None, None, 128)
         qq, kk, vv = (torch.from_numpy(np.ascontiguousarray(x[n])).to(tdt).cuda() for n in ("q", "k", "v"))
         oo = torch.empty_like(qq)
@@ -90,15 +96,27 @@ def main():
         torch.cuda.synchronize()
         d_o = np.abs(oo.double().cpu().numpy() - o_r)
         d_l = np.abs(lse.double().cpu().numpy() - l_r)
-        tb, tc = fa.fa_tile_shape(fa.DTYPE_F16 if fmt == "f16" else fa.DTYPE_F32, 128)
-        rows.append(dict(Br=tb, Bc=tc, default=True, fmt=fmt, order="asc", max_dO=float(d_o.max()),
-                         mean_dO=float(d_o.mean()), max_dLSE=float(d_l.max()), us=float("nan"),
-                         tflops=float("nan")))
-    print("| I/O | order | Br | Bc | max abs dO | mean abs dO | max abs dLSE | us/launch | TFLOP/s |")
-    print("|---|---|---|---|---|---|---|---|---|")
+        tb, tc = fa.fa_tile_shape(fa.DTYPE_F16 if fmt == "f16" else fa.DTYPE_F32, w.d)
+        rows.append(dict(slice=key, d=w.d, Br=tb, Bc=tc, default=True, fmt=fmt, order="asc",
+                         max_dO=float(d_o.max()), mean_dO=float(d_o.mean()),
+                         max_dLSE=float(d_l.max()), us=float("nan"), tflops=float("nan")))
+    return rows
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--json", default=None)
+    ap.add_argument("--reps", type=int, default=20)
+    args = ap.parse_args()
+    rows = []
+    for key, N, H in SLICES:
+        rows += sweep(key, N, H, args.reps, with_orders=True)
+    print("| slice | d | I/O | order | Br | Bc | max abs dO | mean abs dO | max abs dLSE | us/launch | TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         tag = " (default)" if r["default"] else ""
-        print(f"| {r.get('fmt', 'bf16')} | {r['order']} | {r['Br']}{tag} | {r['Bc']} | {r['max_dO']:.3e} | {r['mean_dO']:.3e} | "
+        print(f"| {r['slice']} | {r['d']} | {r.get('fmt', 'bf16')} | {r['order']} | {r['Br']}{tag} | {r['Bc']} | "
+              f"{r['max_dO']:.3e} | {r['mean_dO']:.3e} | "
               f"{r['max_dLSE']:.3e} | {r['us']:.1f} | {r['tflops']:.1f} |", flush=True)
     if args.json:
         with open(args.json, "w") as f:
