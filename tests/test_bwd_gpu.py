@@ -157,3 +157,37 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_gqa_full_size_sampled():
+    # Grouped heads at the 16K causal shape (B1 H16 N16384 d128, four query
+    # heads per key/value head): forward O and LSE on sampled rows, dQ on
+    # sampled rows, dK and dV on sampled keys of one key/value head (summed
+    # over its four query heads by the oracle).
+    B, H, Hkv, N, d = 1, 16, 4, 16384, 128
+    rng = np.random.Generator(np.random.PCG64(3004))
+    q = random_qkv(B, H, N, d, 0, "bf16", 0.5, rng=rng)[0]
+    _, k, v, rng = random_qkv(B, Hkv, N, d, 0, "bf16", 0.5, rng=rng)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    tdo = dev(rng.standard_normal(q.shape, dtype=np.float32))
+    o, lse = fa.fwd(tq, tk, tv, causal=True, scale=scale)
+    dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = rng.choice(B * H * N, size=24, replace=False)
+    cols = int(rng.integers(B * Hkv)) * N + np.unique(np.concatenate([[0, N - 1], rng.choice(N, 6)]))
+    o_ref, l_ref = oracle.attention_rows_f64(q, k, v, rows, scale, True)
+    dout = tdo.float().cpu().numpy()
+    ref = {"dq": oracle.attention_bwd_rows_f64(q, k, v, dout, rows, scale, True)}
+    ref["dk"], ref["dv"] = oracle.attention_bwd_cols_f64(q, k, v, dout, cols, scale, True)
+    rows_t, cols_t = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    o_s = o.reshape(-1, d)[rows_t].double().cpu().numpy()
+    l_s = lse.reshape(-1)[rows_t].double().cpu().numpy()
+    assert np.abs(o_s - o_ref).max() <= 2e-2
+    assert np.abs(l_s - l_ref).max() <= 1e-3
+    got = {"dq": dq.reshape(-1, d)[rows_t], "dk": dk.reshape(-1, d)[cols_t], "dv": dv.reshape(-1, d)[cols_t]}
+    for name, r in ref.items():
+        g = got[name].double().cpu().numpy()
+        err = float(np.abs(g - r).max())
+        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        assert err <= bound, f"GQA {name}: max|dg| = {err:.3e} > {bound:.3e}"
