@@ -10,7 +10,9 @@ Prints ONE JSON line:
               device synchronise on both sides); FLOP = 4*d per visible
               (query, key) pair, masked pairs and softmax not counted
   roofline    the attention kernel's average launch time from HIP events on
-              the launch stream, against the dense bf16 matrix-core peak;
+              the launch stream, against the dense bf16 matrix-core peak
+              (plus the 10th/50th/90th percentile of single launches, from a
+              separate pass after the timed region);
               traffic = measured HBM bytes per launch from the committed
               rocprofv3 counter summary if it was taken on the current
               kernel sources, else null
@@ -204,6 +206,23 @@ def main():
     wall_ms = (t1 - t0) * 1e3 / args.steps
     kern_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # Per-launch spread, measured after the timed region in a pass of its own
+    # (one HIP event pair around each launch, on the launch stream).
+    stream = torch.cuda.current_stream()
+    spread = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(args.steps, 50))]
+    for e0, e1 in spread:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = sorted(e0.elapsed_time(e1) for e0, e1 in spread)
+
+    def pct(p):
+        if not launch_ms:
+            return float("nan")
+        return launch_ms[min(len(launch_ms) - 1, int(round(p / 100 * (len(launch_ms) - 1))))]
+
     pairs = allowed_pairs(w.N, w.B, w.H, w.causal, inp["key_len"], inp["block_mask"])
     flop = 4 * w.d * pairs
     value = flop / (wall_ms * 1e-3) / 1e12
@@ -239,6 +258,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.key),
                      "kernel_ms": round(kern_ms, 5),
+                     "launch_ms_p10_p50_p90": [round(pct(10), 5), round(pct(50), 5), round(pct(90), 5)],
                      "algorithmic_bytes": algorithmic_bytes(w, inp)},
         "cpu_baseline": cpu,
         "max_abs_dO_sampled": dev_o,
