@@ -1,6 +1,6 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (forward,
- * and the backward pass of the bf16 forward).
+ * and the backward pass of the bf16 and fp16 forward).
  *
  * The forward entry points compute, for every batch entry b and head h,
  *
@@ -194,6 +194,20 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            void *dk, void *dv, int B, int H, int H_kv, int N, int d,
            float scale, int causal, const int32_t *key_len,
            const uint8_t *block_mask, hipStream_t stream);
+
+/*
+ * fa_bwd for a chosen element type: dtype FA_DTYPE_BF16 (what fa_bwd does)
+ * or FA_DTYPE_F16 (q, k, v, o, dout, dq, dk, dv all IEEE half; P and dS
+ * enter the matrix-core products rounded to fp16 instead of bf16, every
+ * other step as for bf16).  Other dtypes: FA_ERR_UNSUPPORTED_TILE.  Same
+ * arguments, layouts and behaviour as fa_bwd otherwise; the forward that
+ * produced o and lse is fa_fwd_ex / fa_fwd_gqa with the same dtype.
+ */
+int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o,
+              const void *dout, const float *lse, float *delta, void *dq,
+              void *dk, void *dv, int B, int H, int H_kv, int N, int d,
+              float scale, int causal, const int32_t *key_len,
+              const uint8_t *block_mask, hipStream_t stream, int dtype);
 
 /* Query rows (Br) and key rows (Bc) per tile that fa_fwd_ex would use for
  * (dtype, d, block mask given or not, Br, Bc); writes them to *br_out /

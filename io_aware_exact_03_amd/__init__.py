@@ -1,7 +1,7 @@
 """Python binding of the gfx950 exact-attention library (libfa.so).
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
-``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_tile_shape``,
+``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_bwd_ex``, ``fa_tile_shape``,
 ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
@@ -13,7 +13,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_bwd", "bwd",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "bwd",
            "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING", "ORDER_SHUFFLED",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
            "DTYPE_BF16", "DTYPE_F32", "DTYPE_F16", "MASK_BLOCK"]
@@ -71,6 +71,8 @@ def _load():
     lib.fa_fwd_gqa.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_ex.argtypes = [vp] * 10 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp, i32]
+    lib.fa_bwd_ex.restype = i32
     lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fa_tile_shape.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -124,6 +126,12 @@ def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, ca
            block_mask, stream):
     _check(_load().fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale,
                           int(bool(causal)), key_len, block_mask, stream), "fa_bwd")
+
+
+def fa_bwd_ex(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, causal, key_len,
+              block_mask, stream, dtype):
+    _check(_load().fa_bwd_ex(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale,
+                             int(bool(causal)), key_len, block_mask, stream, dtype), "fa_bwd_ex")
 
 
 def fa_tile_shape(dtype, d, block_sparse=False, Br=0, Bc=0):
@@ -216,17 +224,19 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
 
 def bwd(q, k, v, o, dout, lse, causal=False, key_len=None, block_mask=None, scale=None,
         dq=None, dk=None, dv=None, delta=None, stream=None):
-    """Gradients (dq, dk, dv) of sum(dout * o) for bf16 attention.
+    """Gradients (dq, dk, dv) of sum(dout * o) for bf16 or fp16 attention.
 
-    q, o, dout: contiguous bfloat16 [B, H, N, d] cuda tensors; k, v:
-    [B, H_kv, N, d]; lse: float32 [B, H, N] from ``fwd`` on the same inputs
-    and options.  Outputs (and the float32 [B, H, N] workspace ``delta``)
-    are allocated with torch unless passed in.
+    q, o, dout: contiguous bfloat16 or float16 [B, H, N, d] cuda tensors (one
+    dtype for all); k, v: [B, H_kv, N, d]; lse: float32 [B, H, N] from
+    ``fwd`` on the same inputs and options.  Outputs (and the float32
+    [B, H, N] workspace ``delta``) are allocated with torch unless passed in.
     """
     import torch
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("bwd takes bfloat16 or float16 tensors")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous 4-d bfloat16 cuda tensor")
+        if t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d cuda tensor of q's dtype")
     B, H, N, d = q.shape
     if o.shape != q.shape or dout.shape != q.shape:
         raise ValueError("o and dout must have q's shape")
@@ -241,11 +251,17 @@ def bwd(q, k, v, o, dout, lse, causal=False, key_len=None, block_mask=None, scal
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != q.dtype or t.shape != like.shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous cuda tensor like {'q' if like is q else 'k'}")
+    if delta.dtype != torch.float32 or delta.shape != (B, H, N) or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B, H, N] tensor")
     kl_ptr = key_len.data_ptr() if key_len is not None else None
     bm_ptr = block_mask.data_ptr() if block_mask is not None else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-           delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
-           float(scale), causal, kl_ptr, bm_ptr, stream)
+    fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+              delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
+              float(scale), causal, kl_ptr, bm_ptr, stream,
+              DTYPE_F16 if q.dtype == torch.float16 else DTYPE_BF16)
     return dq, dk, dv

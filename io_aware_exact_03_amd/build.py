@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_bf16_pipe.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_bf16_pipe.hip", "fa_fwd_f32.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -121,10 +121,11 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
 int backward(const void *q, const void *k, const void *v, const void *o, const void *dout,
              const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int H, int Hkv,
              int N, int d, float scale, int causal, const int32_t *key_len,
-             const uint8_t *block_mask, hipStream_t stream) {
+             const uint8_t *block_mask, hipStream_t stream, int dtype) {
     if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
     if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED_TILE;
     const uint64_t groups = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 15) / 16);
     if (groups >= (1ull << 31)) return FA_ERR_INVALID_SHAPE;
     const void *a16[] = {q, k, v, o, dout, dq, dk, dv};
@@ -165,7 +166,7 @@ int backward(const void *q, const void *k, const void *v, const void *o, const v
     a.nkb = (N + 127) / 128;
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    const hipError_t err = fa::launch_bwd(a, d, causal ? 1 : 0, stream);
+    const hipError_t err = fa::launch_bwd(a, d, causal ? 1 : 0, dtype == FA_DTYPE_F16 ? 1 : 0, stream);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return FA_ERR_HIP;
@@ -218,7 +219,15 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int N, int d, float scale, int causal, const int32_t *key_len,
            const uint8_t *block_mask, hipStream_t stream) {
     return backward(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
-                    key_len, block_mask, stream);
+                    key_len, block_mask, stream, FA_DTYPE_BF16);
+}
+
+int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const void *dout,
+              const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int H, int H_kv,
+              int N, int d, float scale, int causal, const int32_t *key_len,
+              const uint8_t *block_mask, hipStream_t stream, int dtype) {
+    return backward(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
+                    key_len, block_mask, stream, dtype);
 }
 
 int fa_tile_shape(int dtype, int d, int block_sparse, int Br, int Bc, int *br_out, int *bc_out) {

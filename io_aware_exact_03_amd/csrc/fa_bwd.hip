@@ -1,5 +1,6 @@
 // Exact-attention backward pass for gfx950: the gradients dQ, dK, dV of the
-// loss sum(dO * O), bf16 inputs and outputs, fp32 accumulation.
+// loss sum(dO * O), bf16 or fp16 inputs and outputs (every kernel is a
+// template on the element type T), fp32 accumulation.
 //
 // The pages give the forward definition (page "Ch.04 Attention
 // optimisation: FlashAttention and sparse attention", mdooai.com, "Core
@@ -73,11 +74,12 @@ struct BwdGeom {
     static constexpr int NCOPY = TILE / 512;
 };
 
-// Copy rows [r0, r0 + ROWS) of a [.., D] bf16 matrix into a swizzled LDS
-// tile (rows >= rows_valid re-read the last valid row: their results are
-// masked).  The NW waves split the 1 KiB copy instructions.
-template <int D, int NW, int ROWS = 32>
-__device__ __forceinline__ void copy_rows(const __bf16 *G, int r0, int rows_valid, __bf16 *dst,
+// Copy rows [r0, r0 + ROWS) of a [.., D] matrix of 16-bit elements (bf16 or
+// fp16) into a swizzled LDS tile (rows >= rows_valid re-read the last valid
+// row: their results are masked).  The NW waves split the 1 KiB copy
+// instructions.  G and dst are byte addresses.
+template <int D, int NW, int ROWS>
+__device__ __forceinline__ void copy_rows(const void *G, int r0, int rows_valid, void *dst,
                                           int wave, int lane) {
     constexpr int SLOTS = D / 8, NCOPY = ROWS * D / 512;
 #pragma unroll
@@ -87,8 +89,8 @@ __device__ __forceinline__ void copy_rows(const __bf16 *G, int r0, int rows_vali
         const int ci = q * 64 + lane;
         const int r = ci / SLOTS, p = ci % SLOTS;
         const int row = min(r0 + r, rows_valid - 1);
-        const __bf16 *src = G + (int64_t)row * D + ((p ^ zkv<D>(r)) << 3);
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst + q * 512),
+        const char *src = static_cast<const char *>(G) + ((int64_t)row * D + ((p ^ zkv<D>(r)) << 3)) * 2;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(static_cast<char *>(dst) + q * 1024),
                                          16, 0, 0);
     }
 }
@@ -108,14 +110,18 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&lo)[D / 32], int (&hi
     }
 }
 
-__device__ __forceinline__ bf16x8_t read_tr8(const __bf16 *base, int lo, int hi) {
+template <class T>
+__device__ __forceinline__ typename Elem<T>::x8 read_tr8(const T *base, int lo, int hi) {
     const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + lo));
     const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(base + hi));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(typename Elem<T>::x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    return Elem<__bf16>::mfma(a, b, c);
+}
+__device__ __forceinline__ f32x16_t mfma(f16x8_t a, f16x8_t b, f32x16_t c) {
+    return Elem<_Float16>::mfma(a, b, c);
 }
 
 // Row of accumulator value i of lane l in a 32x32 product block.
@@ -123,8 +129,10 @@ __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 
 
 // ---------------------------------------------------------------- Delta
 
-template <int D>
+template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
+    using x8_t = typename Elem<T>::x8;
+    using x4_t = typename Elem<T>::x4;
     // 16 lanes (D = 128) or 8 lanes (D = 64) per row, 8 elements each.
     constexpr int LPR = D / 8;
     const int64_t rows = (int64_t)a.B * a.H * a.N;
@@ -132,10 +140,10 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
     const int part = threadIdx.x % LPR;
     float acc = 0.f;
     if (row < rows) {
-        const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(
-            reinterpret_cast<const __bf16 *>(a.o) + row * D + part * 8);
-        const bf16x8_t y = *reinterpret_cast<const bf16x8_t *>(
-            reinterpret_cast<const __bf16 *>(a.dout) + row * D + part * 8);
+        const x8_t x = *reinterpret_cast<const x8_t *>(
+            reinterpret_cast<const T *>(a.o) + row * D + part * 8);
+        const x8_t y = *reinterpret_cast<const x8_t *>(
+            reinterpret_cast<const T *>(a.dout) + row * D + part * 8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc = fmaf((float)x[j], (float)y[j], acc);
     }
@@ -146,15 +154,17 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, int NW, int QT, bool CAUSAL>
+template <class T, int D, int NW, int QT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
+    using x8_t = typename Elem<T>::x8;
+    using x4_t = typename Elem<T>::x4;
     using Geo = BwdGeom<D>;
     constexpr int NQK = Geo::NQK, ND = Geo::ND, BK = 32 * NW, BQ = 32 * QT;
     static_assert(128 % BQ == 0, "a query tile lies inside one 128-row mask block");
     // Q and dO tiles of BQ rows, and the tile's LSE and Delta (BQ floats
     // each, LSE first), double-buffered.
-    __shared__ __attribute__((aligned(1024))) __bf16 q_lds[2][BQ * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 do_lds[2][BQ * D];
+    __shared__ __attribute__((aligned(1024))) T q_lds[2][BQ * D];
+    __shared__ __attribute__((aligned(1024))) T do_lds[2][BQ * D];
     __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * BQ];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -175,15 +185,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     int kv_len = N;
     if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
     const int64_t kvhead = (int64_t)bkv * N * D;
-    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + kvhead;
-    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + kvhead;
+    const T *K = reinterpret_cast<const T *>(a.k) + kvhead;
+    const T *V = reinterpret_cast<const T *>(a.v) + kvhead;
     const float c = a.scale_log2;
     const bool wave_live = kw0 < kv_len;  // keys >= kv_len get zero gradients
 
     // This wave's 32 keys as B operands: K^T and V^T fragments (lane: key
     // lane % 32, head dims 16*ks + 8*(lane/32) .. +7).
     const int key = kw0 + lane % 32;
-    bf16x8_t kf[NQK], vf[NQK];
+    x8_t kf[NQK], vf[NQK];
 #pragma unroll
     for (int ks = 0; ks < NQK; ++ks) {
         u32x4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
@@ -191,8 +201,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
             xk = *reinterpret_cast<const u32x4_t *>(K + (int64_t)key * D + ks * 16 + 8 * (lane / 32));
             xv = *reinterpret_cast<const u32x4_t *>(V + (int64_t)key * D + ks * 16 + 8 * (lane / 32));
         }
-        kf[ks] = __builtin_bit_cast(bf16x8_t, xk);
-        vf[ks] = __builtin_bit_cast(bf16x8_t, xv);
+        kf[ks] = __builtin_bit_cast(x8_t, xk);
+        vf[ks] = __builtin_bit_cast(x8_t, xv);
     }
     f32x16_t dk[ND], dv[ND];
 #pragma unroll
@@ -223,9 +233,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
         int hq, qt;
         step_tile(s, &hq, &qt);
         const int64_t qhead = (int64_t)hq * N * D;
-        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.q) + qhead, qt * BQ, N, q_lds[buf], wave,
+        copy_rows<D, NW, BQ>(reinterpret_cast<const T *>(a.q) + qhead, qt * BQ, N, q_lds[buf], wave,
                              lane);
-        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.dout) + qhead, qt * BQ, N, do_lds[buf],
+        copy_rows<D, NW, BQ>(reinterpret_cast<const T *>(a.dout) + qhead, qt * BQ, N, do_lds[buf],
                              wave, lane);
         // LSE and Delta of the tile's rows (4 bytes per lane; clamped rows
         // past N are masked).
@@ -263,15 +273,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
 #pragma unroll
         for (int hq32 = 0; hq32 < QT; ++hq32) {
             const int qs = qs0 + 32 * hq32;
-            const __bf16 *Qs = q_lds[buf] + hq32 * 32 * D, *dOs = do_lds[buf] + hq32 * 32 * D;
+            const T *Qs = q_lds[buf] + hq32 * 32 * D, *dOs = do_lds[buf] + hq32 * 32 * D;
             // this wave's keys see some query of these 32 rows
             if (wave_live && (!CAUSAL || qs + 31 >= kw0)) {
                 // S = Q K^T and dP = dO V^T: D[m = query][n = key].
                 f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
                 for (int ks = 0; ks < NQK; ++ks) {
-                    const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(Qs + (rbase ^ (ks << 4)));
-                    const bf16x8_t da = *reinterpret_cast<const bf16x8_t *>(dOs + (rbase ^ (ks << 4)));
+                    const x8_t qa = *reinterpret_cast<const x8_t *>(Qs + (rbase ^ (ks << 4)));
+                    const x8_t da = *reinterpret_cast<const x8_t *>(dOs + (rbase ^ (ks << 4)));
                     sacc = mfma(qa, kf[ks], sacc);
                     dpacc = mfma(da, vf[ks], dpacc);
                 }
@@ -301,16 +311,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
                 // dV^T += dO^T P^T and dK^T += Q^T dS^T over the two 16-row chunks.
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    bf16x8_t pf, dsf;
+                    x8_t pf, dsf;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        pf[j] = (__bf16)sacc[8 * h + j];
-                        dsf[j] = (__bf16)dpacc[8 * h + j];
+                        pf[j] = (T)sacc[8 * h + j];
+                        dsf[j] = (T)dpacc[8 * h + j];
                     }
 #pragma unroll
                     for (int mb = 0; mb < ND; ++mb) {
-                        const bf16x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
-                        const bf16x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
+                        const x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
+                        const x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
                         dv[mb] = mfma(dot, pf, dv[mb]);
                         dk[mb] = mfma(qtr, dsf, dk[mb]);
                     }
@@ -325,20 +335,20 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     // 32*mb + 8*gg + 4*(lane/32) .. +3.
     if (key < N) {
         const float scale = a.scale;
-        __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + kvhead + (int64_t)key * D;
-        __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + kvhead + (int64_t)key * D;
+        T *dK = reinterpret_cast<T *>(a.dk) + kvhead + (int64_t)key * D;
+        T *dV = reinterpret_cast<T *>(a.dv) + kvhead + (int64_t)key * D;
 #pragma unroll
         for (int mb = 0; mb < ND; ++mb)
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
-                bf16x4_t wk, wv;
+                x4_t wk, wv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    wk[j] = (__bf16)(dk[mb][4 * gg + j] * scale);
-                    wv[j] = (__bf16)dv[mb][4 * gg + j];
+                    wk[j] = (T)(dk[mb][4 * gg + j] * scale);
+                    wv[j] = (T)dv[mb][4 * gg + j];
                 }
-                *reinterpret_cast<bf16x4_t *>(dK + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
-                *reinterpret_cast<bf16x4_t *>(dV + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
+                *reinterpret_cast<x4_t *>(dK + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
+                *reinterpret_cast<x4_t *>(dV + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
             }
     }
 }
@@ -349,8 +359,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
 // its K fragments and its dK^T, dV^T accumulators in registers (V fragments
 // come from the key block's K/V tiles, loaded into LDS once).  The two
 // partial sums of each key group are added through LDS at the end.
-template <int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a) {
+    using x8_t = typename Elem<T>::x8;
+    using x4_t = typename Elem<T>::x4;
     using Geo = BwdGeom<D>;
     constexpr int NQK = Geo::NQK, ND = Geo::ND, NW = 8, BK = 128, BQ = 64;
     constexpr int KV_BYTES = BK * D * 2, T_BYTES = BQ * D * 2;
@@ -358,10 +370,10 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     constexpr int POOL = 2 * KV_BYTES + 4 * T_BYTES > RED_BYTES ? 2 * KV_BYTES + 4 * T_BYTES : RED_BYTES;
     __shared__ __attribute__((aligned(1024))) char pool[POOL];
     __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * BQ];
-    __bf16 *const k_lds = reinterpret_cast<__bf16 *>(pool);
-    __bf16 *const v_lds = reinterpret_cast<__bf16 *>(pool + KV_BYTES);
-    auto q_lds = [&](int buf) { return reinterpret_cast<__bf16 *>(pool + 2 * KV_BYTES + buf * T_BYTES); };
-    auto do_lds = [&](int buf) { return reinterpret_cast<__bf16 *>(pool + 2 * KV_BYTES + (2 + buf) * T_BYTES); };
+    T *const k_lds = reinterpret_cast<T *>(pool);
+    T *const v_lds = reinterpret_cast<T *>(pool + KV_BYTES);
+    auto q_lds = [&](int buf) { return reinterpret_cast<T *>(pool + 2 * KV_BYTES + buf * T_BYTES); };
+    auto do_lds = [&](int buf) { return reinterpret_cast<T *>(pool + 2 * KV_BYTES + (2 + buf) * T_BYTES); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -385,8 +397,8 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     const int key = kw0 + lane % 32;
 
     // The key block's K and V rows into LDS (rows past N re-read row N-1).
-    copy_rows<D, NW, BK>(reinterpret_cast<const __bf16 *>(a.k) + kvhead, k0, N, k_lds, wave, lane);
-    copy_rows<D, NW, BK>(reinterpret_cast<const __bf16 *>(a.v) + kvhead, k0, N, v_lds, wave, lane);
+    copy_rows<D, NW, BK>(reinterpret_cast<const T *>(a.k) + kvhead, k0, N, k_lds, wave, lane);
+    copy_rows<D, NW, BK>(reinterpret_cast<const T *>(a.v) + kvhead, k0, N, v_lds, wave, lane);
 
     const int rbase = (lane % 32) * D + (((lane / 32) ^ zkv<D>(lane % 32)) << 3);
     int trlo[ND], trhi[ND];
@@ -414,8 +426,8 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
         int hq, qt;
         step_tile(s, &hq, &qt);
         const int64_t qhead = (int64_t)hq * N * D;
-        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.q) + qhead, qt * BQ, N, q_lds(buf), wave, lane);
-        copy_rows<D, NW, BQ>(reinterpret_cast<const __bf16 *>(a.dout) + qhead, qt * BQ, N, do_lds(buf), wave,
+        copy_rows<D, NW, BQ>(reinterpret_cast<const T *>(a.q) + qhead, qt * BQ, N, q_lds(buf), wave, lane);
+        copy_rows<D, NW, BQ>(reinterpret_cast<const T *>(a.dout) + qhead, qt * BQ, N, do_lds(buf), wave,
                              lane);
         if (wave < 2) {
             const int idx = wave * 64 + lane;
@@ -440,10 +452,10 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     wait_copies();
     __syncthreads();
     // This wave's K^T fragments (B operand of S = Q K^T), kept in registers.
-    bf16x8_t kf[NQK];
-    const __bf16 *kg_k = k_lds + kg * 32 * D, *kg_v = v_lds + kg * 32 * D;
+    x8_t kf[NQK];
+    const T *kg_k = k_lds + kg * 32 * D, *kg_v = v_lds + kg * 32 * D;
 #pragma unroll
-    for (int ks = 0; ks < NQK; ++ks) kf[ks] = *reinterpret_cast<const bf16x8_t *>(kg_k + (rbase ^ (ks << 4)));
+    for (int ks = 0; ks < NQK; ++ks) kf[ks] = *reinterpret_cast<const x8_t *>(kg_k + (rbase ^ (ks << 4)));
 
     int buf = 0;
     while (s < nsteps) {
@@ -454,15 +466,15 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
         int hq, qt;
         step_tile(s, &hq, &qt);
         const int qs = qt * BQ + 32 * qh;
-        const __bf16 *Qs = q_lds(buf) + qh * 32 * D, *dOs = do_lds(buf) + qh * 32 * D;
+        const T *Qs = q_lds(buf) + qh * 32 * D, *dOs = do_lds(buf) + qh * 32 * D;
         const float *lds_l = ld_lds[buf];
         if (wave_live && (!CAUSAL || qs + 31 >= kw0)) {
             f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
             for (int ks = 0; ks < NQK; ++ks) {
-                const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(Qs + (rbase ^ (ks << 4)));
-                const bf16x8_t da = *reinterpret_cast<const bf16x8_t *>(dOs + (rbase ^ (ks << 4)));
-                const bf16x8_t vb = *reinterpret_cast<const bf16x8_t *>(kg_v + (rbase ^ (ks << 4)));
+                const x8_t qa = *reinterpret_cast<const x8_t *>(Qs + (rbase ^ (ks << 4)));
+                const x8_t da = *reinterpret_cast<const x8_t *>(dOs + (rbase ^ (ks << 4)));
+                const x8_t vb = *reinterpret_cast<const x8_t *>(kg_v + (rbase ^ (ks << 4)));
                 sacc = mfma(qa, kf[ks], sacc);
                 dpacc = mfma(da, vb, dpacc);
             }
@@ -488,16 +500,16 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                bf16x8_t pf, dsf;
+                x8_t pf, dsf;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    pf[j] = (__bf16)sacc[8 * h + j];
-                    dsf[j] = (__bf16)dpacc[8 * h + j];
+                    pf[j] = (T)sacc[8 * h + j];
+                    dsf[j] = (T)dpacc[8 * h + j];
                 }
 #pragma unroll
                 for (int mb = 0; mb < ND; ++mb) {
-                    const bf16x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
-                    const bf16x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
+                    const x8_t dot = read_tr8(dOs + h * 16 * D, trlo[mb], trhi[mb]);
+                    const x8_t qtr = read_tr8(Qs + h * 16 * D, trlo[mb], trhi[mb]);
                     dv[mb] = mfma(dot, pf, dv[mb]);
                     dk[mb] = mfma(qtr, dsf, dk[mb]);
                 }
@@ -529,35 +541,37 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     __syncthreads();
     if (qh == 0 && key < N) {
         const float scale = a.scale;
-        __bf16 *dK = reinterpret_cast<__bf16 *>(a.dk) + kvhead + (int64_t)key * D;
-        __bf16 *dV = reinterpret_cast<__bf16 *>(a.dv) + kvhead + (int64_t)key * D;
+        T *dK = reinterpret_cast<T *>(a.dk) + kvhead + (int64_t)key * D;
+        T *dV = reinterpret_cast<T *>(a.dv) + kvhead + (int64_t)key * D;
 #pragma unroll
         for (int mb = 0; mb < ND; ++mb)
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
                 const f32x4_t xk = red[((2 * mb) * 4 + gg) * 64 + lane];
                 const f32x4_t xv = red[((2 * mb + 1) * 4 + gg) * 64 + lane];
-                bf16x4_t wk, wv;
+                x4_t wk, wv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    wk[j] = (__bf16)((dk[mb][4 * gg + j] + xk[j]) * scale);
-                    wv[j] = (__bf16)(dv[mb][4 * gg + j] + xv[j]);
+                    wk[j] = (T)((dk[mb][4 * gg + j] + xk[j]) * scale);
+                    wv[j] = (T)(dv[mb][4 * gg + j] + xv[j]);
                 }
-                *reinterpret_cast<bf16x4_t *>(dK + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
-                *reinterpret_cast<bf16x4_t *>(dV + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
+                *reinterpret_cast<x4_t *>(dK + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
+                *reinterpret_cast<x4_t *>(dV + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
             }
     }
 }
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, int NW, int KT, bool CAUSAL>
+template <class T, int D, int NW, int KT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
+    using x8_t = typename Elem<T>::x8;
+    using x4_t = typename Elem<T>::x4;
     using Geo = BwdGeom<D>;
     constexpr int NQK = Geo::NQK, ND = Geo::ND, BR = 32 * NW, BKT = 32 * KT;
     static_assert(128 % BKT == 0, "a key step lies inside one 128-key mask block");
-    __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2][KT * Geo::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2][KT * Geo::TILE];
+    __shared__ __attribute__((aligned(1024))) T k_lds[2][KT * Geo::TILE];
+    __shared__ __attribute__((aligned(1024))) T v_lds[2][KT * Geo::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -568,10 +582,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
-    const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q) + head;
-    const __bf16 *dO = reinterpret_cast<const __bf16 *>(a.dout) + head;
-    const __bf16 *K = reinterpret_cast<const __bf16 *>(a.k) + kvhead;
-    const __bf16 *V = reinterpret_cast<const __bf16 *>(a.v) + kvhead;
+    const T *Q = reinterpret_cast<const T *>(a.q) + head;
+    const T *dO = reinterpret_cast<const T *>(a.dout) + head;
+    const T *K = reinterpret_cast<const T *>(a.k) + kvhead;
+    const T *V = reinterpret_cast<const T *>(a.v) + kvhead;
     const float c = a.scale_log2;
 
     const int q0 = qt * BR, wq0 = q0 + wave * 32;
@@ -583,7 +597,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     const int ntiles = (kv_end + BKT - 1) / BKT;
 
     // This wave's 32 query rows as B operands: Q^T and dO^T fragments.
-    bf16x8_t qf[NQK], dof[NQK];
+    x8_t qf[NQK], dof[NQK];
 #pragma unroll
     for (int ks = 0; ks < NQK; ++ks) {
         u32x4_t xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
@@ -591,8 +605,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
             xq = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
             xd = *reinterpret_cast<const u32x4_t *>(dO + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
         }
-        qf[ks] = __builtin_bit_cast(bf16x8_t, xq);
-        dof[ks] = __builtin_bit_cast(bf16x8_t, xd);
+        qf[ks] = __builtin_bit_cast(x8_t, xq);
+        dof[ks] = __builtin_bit_cast(x8_t, xd);
     }
     float lse2 = __builtin_inff(), dl = 0.f;
     if (qrow < N) {
@@ -636,14 +650,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
 #pragma unroll 1
         for (int kc = 0; kc < KT; ++kc) {
             const int kbase = t * BKT + 32 * kc;
-            const __bf16 *Ks = k_lds[buf] + kc * Geo::TILE, *Vs = v_lds[buf] + kc * Geo::TILE;
+            const T *Ks = k_lds[buf] + kc * Geo::TILE, *Vs = v_lds[buf] + kc * Geo::TILE;
             if (wq0 < N && kbase < kv_end && (!CAUSAL || kbase <= wq0 + 31)) {
                 // S^T = K Q^T and dP^T = V dO^T: D[m = key][n = query].
                 f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
                 for (int ks = 0; ks < NQK; ++ks) {
-                    const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(Ks + (rbase ^ (ks << 4)));
-                    const bf16x8_t va = *reinterpret_cast<const bf16x8_t *>(Vs + (rbase ^ (ks << 4)));
+                    const x8_t ka = *reinterpret_cast<const x8_t *>(Ks + (rbase ^ (ks << 4)));
+                    const x8_t va = *reinterpret_cast<const x8_t *>(Vs + (rbase ^ (ks << 4)));
                     sacc = mfma(ka, qf[ks], sacc);
                     dpacc = mfma(va, dof[ks], dpacc);
                 }
@@ -662,12 +676,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
                 // dQ^T += K^T dS^T over the two 16-key chunks.
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    bf16x8_t dsf;
+                    x8_t dsf;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) dsf[j] = (__bf16)ds[8 * h + j];
+                    for (int j = 0; j < 8; ++j) dsf[j] = (T)ds[8 * h + j];
 #pragma unroll
                     for (int mb = 0; mb < ND; ++mb) {
-                        const bf16x8_t ktr = read_tr8(Ks + h * 16 * D, trlo[mb], trhi[mb]);
+                        const x8_t ktr = read_tr8(Ks + h * 16 * D, trlo[mb], trhi[mb]);
                         dq[mb] = mfma(ktr, dsf, dq[mb]);
                     }
                 }
@@ -679,25 +693,25 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
 
     if (qrow < N) {
         const float scale = a.scale;
-        __bf16 *dQ = reinterpret_cast<__bf16 *>(a.dq) + head + (int64_t)qrow * D;
+        T *dQ = reinterpret_cast<T *>(a.dq) + head + (int64_t)qrow * D;
 #pragma unroll
         for (int mb = 0; mb < ND; ++mb)
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
-                bf16x4_t w;
+                x4_t w;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) w[j] = (__bf16)(dq[mb][4 * gg + j] * scale);
-                *reinterpret_cast<bf16x4_t *>(dQ + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
+                for (int j = 0; j < 4; ++j) w[j] = (T)(dq[mb][4 * gg + j] * scale);
+                *reinterpret_cast<x4_t *>(dQ + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
             }
     }
 }
 
-template <int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL>
 hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     constexpr int NW = 4;
     const int64_t rows = (int64_t)a.B * a.H * a.N;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_delta<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkt = (a.N + 32 * NW - 1) / (32 * NW);
@@ -705,25 +719,31 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     // workgroups per CU (128 rows would spill)
     constexpr int QT = 2;
     if constexpr (D == 128 || CAUSAL)
-        hipLaunchKernelGGL((bwd_dkdv_pair<D, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0, stream,
+        hipLaunchKernelGGL((bwd_dkdv_pair<T, D, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0, stream,
                            a);
     else
-        hipLaunchKernelGGL((bwd_dkdv<D, NW, QT, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64),
+        hipLaunchKernelGGL((bwd_dkdv<T, D, NW, QT, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64),
                            0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
     constexpr int KT = 2;
-    hipLaunchKernelGGL((bwd_dq<D, NW, KT, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dq<T, D, NW, KT, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream,
                        a);
     return hipGetLastError();
 }
 
+template <class T>
+hipError_t launch_bwd_typed(const BwdArgs &a, int d, int causal, hipStream_t stream) {
+    if (d == 64)
+        return causal ? launch_bwd_impl<T, 64, true>(a, stream) : launch_bwd_impl<T, 64, false>(a, stream);
+    return causal ? launch_bwd_impl<T, 128, true>(a, stream) : launch_bwd_impl<T, 128, false>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs &a, int d, int causal, hipStream_t stream) {
-    if (d == 64) return causal ? launch_bwd_impl<64, true>(a, stream) : launch_bwd_impl<64, false>(a, stream);
-    return causal ? launch_bwd_impl<128, true>(a, stream) : launch_bwd_impl<128, false>(a, stream);
+hipError_t launch_bwd(const BwdArgs &a, int d, int causal, int f16, hipStream_t stream) {
+    return f16 ? launch_bwd_typed<_Float16>(a, d, causal, stream) : launch_bwd_typed<__bf16>(a, d, causal, stream);
 }
 
 }  // namespace fa

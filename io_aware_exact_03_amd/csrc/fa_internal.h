@@ -41,7 +41,7 @@ struct BwdArgs {
 };
 
 // Enqueues the three backward kernels on `stream`.
-hipError_t launch_bwd(const BwdArgs &a, int d, int causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int d, int causal, int f16, hipStream_t stream);
 
 // Enqueues one forward pass on `stream`; returns the launch status.
 using Launcher = hipError_t (*)(const FwdArgs &, hipStream_t);

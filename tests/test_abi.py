@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study",
-                                           "fa_fwd_gqa", "fa_bwd", "fa_tile_shape",
+                                           "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "fa_tile_shape",
                                            "fa_status_string", "fa_last_hip_error"])
 
 
@@ -126,16 +126,28 @@ DO, LSEB, DELTA, DQ, DK, DV = 0x60000000, 0x70000000, 0x71000000, 0x72000000, 0x
     (dict(dk=DV + 16), 7),                 # outputs overlapping each other
     (dict(delta=LSEB + 4), 7),             # workspace over the logsumexp
 ])
-def test_bwd_invalid_arguments_return_status_without_launch(kw, status):
+@pytest.mark.parametrize("entry", ["fa_bwd", "fa_bwd_ex"])
+def test_bwd_invalid_arguments_return_status_without_launch(kw, status, entry):
     args = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=LSEB, delta=DELTA, dq=DQ, dk=DK, dv=DV, B=2, H=4,
                 H_kv=2, N=100, d=64, scale=0.125, causal=0, key_len=None, block_mask=None,
                 stream=None)
     args.update(kw)
     lib = fa._load()
-    rc = lib.fa_bwd(*[args[n] for n in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv",
-                                         "B", "H", "H_kv", "N", "d", "scale", "causal", "key_len",
-                                         "block_mask", "stream")])
+    names = ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv", "B", "H", "H_kv", "N", "d",
+             "scale", "causal", "key_len", "block_mask", "stream")
+    if entry == "fa_bwd":
+        rc = lib.fa_bwd(*[args[n] for n in names])
+    else:
+        rc = lib.fa_bwd_ex(*[args[n] for n in names], fa.DTYPE_F16)
     assert rc == status
+
+
+@pytest.mark.parametrize("dtype", [fa.DTYPE_F32, 3, -1])
+def test_bwd_ex_rejects_unbuilt_dtypes(dtype):
+    lib = fa._load()
+    rc = lib.fa_bwd_ex(Q, K, V, O, DO, LSEB, DELTA, DQ, DK, DV, 2, 4, 2, 100, 64, 0.125, 0, None, None,
+                       None, dtype)
+    assert rc == 5
 
 
 def test_status_strings_cover_every_code():

@@ -22,6 +22,10 @@ from workloads import WORKLOADS, make_inputs, random_qkv, band_global_block_mask
 pytestmark = pytest.mark.gpu
 
 TOL_REL = 2e-2
+# fp16 I/O: P, dS and the gradients are rounded to fp16 (relative 2^-11,
+# four times finer than bf16's 2^-9), and O and dO carry fp16 rounding; the
+# bf16 bar scaled by the same 2^-2, rounded up to one significant digit.
+TOL_REL_F16 = 5e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -30,17 +34,18 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def dev(x):
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).cuda()
+def dev(x, dtype="bf16"):
+    t = torch.bfloat16 if dtype == "bf16" else torch.float16
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(t).cuda()
 
 
-def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None, scale=None):
-    q, _, _, rng = random_qkv(B, H, N, d, seed, "bf16")
-    _, k, v, rng = random_qkv(B, H_kv, N, d, seed + 1, "bf16", rng=rng)
+def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None, scale=None,
+             dtype="bf16"):
+    q, _, _, rng = random_qkv(B, H, N, d, seed, dtype)
+    _, k, v, rng = random_qkv(B, H_kv, N, d, seed + 1, dtype, rng=rng)
     dout = rng.standard_normal(q.shape).astype(np.float32)
-    dout = dout.astype(np.float32)
     scale = np.float32(1.0 / math.sqrt(d) if scale is None else scale)
-    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(dout)
+    tq, tk, tv, tdo = dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(dout, dtype)
     dout_b = tdo.float().cpu().numpy()
     kl = torch.from_numpy(np.asarray(key_len, dtype=np.int32)).cuda() if key_len is not None else None
     bm = torch.from_numpy(np.asarray(block_mask, dtype=np.uint8)).cuda() if block_mask is not None else None
@@ -60,7 +65,7 @@ def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None
         assert np.all(np.isfinite(g)), f"{name}: non-finite"
         err = float(np.abs(g - r).max())
         errs[name] = err
-        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        bound = (TOL_REL if dtype == "bf16" else TOL_REL_F16) * max(1.0, float(np.abs(r).max()))
         assert err <= bound, f"{name}: max|dg| = {err:.3e} > {bound:.3e}"
     return errs
 
@@ -83,6 +88,18 @@ def modes(N, seed):
 @pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
 def test_bwd_modes(d, N, mode):
     run_case(2, 2, 2, N, d, seed=70 + N + d, **modes(N, 71)[mode])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [45, 300])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_bwd_f16_modes(d, N, mode):
+    run_case(2, 2, 2, N, d, seed=90 + N + d, dtype="f16", **modes(N, 91)[mode])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f16_grouped_heads(causal):
+    run_case(1, 8, 2, 257, 128, seed=92, causal=causal, dtype="f16")
 
 
 @pytest.mark.parametrize("d", [64, 128])
