@@ -56,6 +56,7 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -196,18 +197,37 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            const uint8_t *block_mask, hipStream_t stream);
 
 /*
- * fa_bwd for a chosen element type: dtype FA_DTYPE_BF16 (what fa_bwd does)
- * or FA_DTYPE_F16 (q, k, v, o, dout, dq, dk, dv all IEEE half; P and dS
- * enter the matrix-core products rounded to fp16 instead of bf16, every
- * other step as for bf16).  Other dtypes: FA_ERR_UNSUPPORTED_TILE.  Same
- * arguments, layouts and behaviour as fa_bwd otherwise; the forward that
- * produced o and lse is fa_fwd_ex / fa_fwd_gqa with the same dtype.
+ * fa_bwd with an element type and an optional workspace.
+ *   dtype     : FA_DTYPE_BF16 (what fa_bwd does) or FA_DTYPE_F16 (q, k, v,
+ *               o, dout, dq, dk, dv all IEEE half; P and dS enter the
+ *               matrix-core products rounded to fp16 instead of bf16, every
+ *               other step as for bf16).  Other dtypes:
+ *               FA_ERR_UNSUPPORTED_TILE.
+ *   workspace : DEVICE memory owned by the caller (16-byte aligned) of
+ *               workspace_bytes bytes, or NULL.  With grouped heads and a
+ *               small key/value grid (few key/value heads, short N), the
+ *               query heads of each group are then split over several
+ *               workgroups that write fp32 partial dK, dV here; a second
+ *               kernel adds them in a fixed order (deterministic) and rounds
+ *               once.  fa_bwd_workspace_size gives the bytes needed; when it
+ *               is 0, or workspace is NULL, no workspace is used and the
+ *               result is that of fa_bwd.  A non-NULL workspace smaller than
+ *               needed, misaligned, or overlapping an input or output:
+ *               FA_ERR_INVALID_ARG.  Its contents on entry do not matter and
+ *               are overwritten.
+ * Same arguments, layouts and behaviour as fa_bwd otherwise; the forward
+ * that produced o and lse is fa_fwd_ex / fa_fwd_gqa with the same dtype.
  */
 int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o,
               const void *dout, const float *lse, float *delta, void *dq,
               void *dk, void *dv, int B, int H, int H_kv, int N, int d,
               float scale, int causal, const int32_t *key_len,
-              const uint8_t *block_mask, hipStream_t stream, int dtype);
+              const uint8_t *block_mask, hipStream_t stream, int dtype,
+              void *workspace, size_t workspace_bytes);
+
+/* Workspace bytes fa_bwd_ex uses for this shape (0: none is used, or the
+ * shape is invalid).  Independent of dtype and masks. */
+size_t fa_bwd_workspace_size(int B, int H, int H_kv, int N, int d);
 
 /* Query rows (Br) and key rows (Bc) per tile that fa_fwd_ex would use for
  * (dtype, d, block mask given or not, Br, Bc); writes them to *br_out /

@@ -1,7 +1,8 @@
 """Python binding of the gfx950 exact-attention library (libfa.so).
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
-``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_bwd_ex``, ``fa_tile_shape``,
+``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_bwd_ex``,
+``fa_bwd_workspace_size``, ``fa_tile_shape``,
 ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
@@ -13,7 +14,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "bwd",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "bwd",
            "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING", "ORDER_SHUFFLED",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
            "DTYPE_BF16", "DTYPE_F32", "DTYPE_F16", "MASK_BLOCK"]
@@ -71,8 +72,11 @@ def _load():
     lib.fa_fwd_gqa.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp]
     lib.fa_bwd.restype = i32
-    lib.fa_bwd_ex.argtypes = [vp] * 10 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp, i32]
+    lib.fa_bwd_ex.argtypes = [vp] * 10 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp, i32, vp,
+                                                       ctypes.c_size_t]
     lib.fa_bwd_ex.restype = i32
+    lib.fa_bwd_workspace_size.argtypes = [i32] * 5
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fa_tile_shape.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -129,9 +133,14 @@ def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, ca
 
 
 def fa_bwd_ex(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, causal, key_len,
-              block_mask, stream, dtype):
+              block_mask, stream, dtype, workspace, workspace_bytes):
     _check(_load().fa_bwd_ex(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale,
-                             int(bool(causal)), key_len, block_mask, stream, dtype), "fa_bwd_ex")
+                             int(bool(causal)), key_len, block_mask, stream, dtype, workspace,
+                             workspace_bytes), "fa_bwd_ex")
+
+
+def fa_bwd_workspace_size(B, H, H_kv, N, d):
+    return int(_load().fa_bwd_workspace_size(B, H, H_kv, N, d))
 
 
 def fa_tile_shape(dtype, d, block_sparse=False, Br=0, Bc=0):
@@ -223,13 +232,16 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
 
 
 def bwd(q, k, v, o, dout, lse, causal=False, key_len=None, block_mask=None, scale=None,
-        dq=None, dk=None, dv=None, delta=None, stream=None):
+        dq=None, dk=None, dv=None, delta=None, stream=None, workspace=True):
     """Gradients (dq, dk, dv) of sum(dout * o) for bf16 or fp16 attention.
 
     q, o, dout: contiguous bfloat16 or float16 [B, H, N, d] cuda tensors (one
     dtype for all); k, v: [B, H_kv, N, d]; lse: float32 [B, H, N] from
     ``fwd`` on the same inputs and options.  Outputs (and the float32
     [B, H, N] workspace ``delta``) are allocated with torch unless passed in.
+    ``workspace``: True allocates the split workspace that
+    ``fa_bwd_workspace_size`` asks for (grouped heads on small grids), a
+    uint8 cuda tensor is used as it, None or False runs without one.
     """
     import torch
     if q.dtype not in (torch.bfloat16, torch.float16):
@@ -260,8 +272,19 @@ def bwd(q, k, v, o, dout, lse, causal=False, key_len=None, block_mask=None, scal
     bm_ptr = block_mask.data_ptr() if block_mask is not None else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws_ptr, ws_bytes = None, 0
+    if workspace is True:
+        need = fa_bwd_workspace_size(B, H, H_kv, N, d)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        else:
+            workspace = None
+    if workspace is not None and workspace is not False:
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 cuda tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
               delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
               float(scale), causal, kl_ptr, bm_ptr, stream,
-              DTYPE_F16 if q.dtype == torch.float16 else DTYPE_BF16)
+              DTYPE_F16 if q.dtype == torch.float16 else DTYPE_BF16, ws_ptr, ws_bytes)
     return dq, dk, dv

@@ -121,7 +121,8 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
 int backward(const void *q, const void *k, const void *v, const void *o, const void *dout,
              const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int H, int Hkv,
              int N, int d, float scale, int causal, const int32_t *key_len,
-             const uint8_t *block_mask, hipStream_t stream, int dtype) {
+             const uint8_t *block_mask, hipStream_t stream, int dtype, void *workspace = nullptr,
+             size_t workspace_bytes = 0) {
     if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
     if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -138,12 +139,19 @@ int backward(const void *q, const void *k, const void *v, const void *o, const v
     // outputs and the workspace must not overlap any input or each other
     const struct { const void *p; uint64_t n; } ins[] = {{q, qb}, {k, kvb}, {v, kvb}, {o, qb}, {dout, qb},
                                                          {lse, rb}};
-    const struct { const void *p; uint64_t n; } outs[] = {{dq, qb}, {dk, kvb}, {dv, kvb}, {delta, rb}};
+    // A workspace is used only when the shape gains from a query-head split
+    // (fa::bwd_workspace_bytes > 0); given but too small is an error.
+    const uint64_t need = fa::bwd_workspace_bytes(B, H, Hkv, N, d);
+    const bool split = workspace && need > 0;
+    if (split && (workspace_bytes < need || !aligned(workspace, 16))) return FA_ERR_INVALID_ARG;
+    const struct { const void *p; uint64_t n; } outs[] = {{dq, qb}, {dk, kvb}, {dv, kvb}, {delta, rb},
+                                                          {split ? workspace : nullptr, split ? need : 0}};
     for (const auto &w : outs) {
+        if (!w.p) continue;
         for (const auto &r : ins)
             if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
         for (const auto &w2 : outs)
-            if (&w2 != &w && overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_INVALID_ARG;
+            if (&w2 != &w && w2.p && overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_INVALID_ARG;
     }
     fa::BwdArgs a;
     a.q = q;
@@ -166,6 +174,8 @@ int backward(const void *q, const void *k, const void *v, const void *o, const v
     a.nkb = (N + 127) / 128;
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.nsplit = split ? fa::bwd_split(B, H, Hkv, N) : 1;
+    a.part = split ? static_cast<float *>(workspace) : nullptr;
     const hipError_t err = fa::launch_bwd(a, d, causal ? 1 : 0, dtype == FA_DTYPE_F16 ? 1 : 0, stream);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
@@ -225,9 +235,15 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
 int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const void *dout,
               const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int H, int H_kv,
               int N, int d, float scale, int causal, const int32_t *key_len,
-              const uint8_t *block_mask, hipStream_t stream, int dtype) {
+              const uint8_t *block_mask, hipStream_t stream, int dtype, void *workspace,
+              size_t workspace_bytes) {
     return backward(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
-                    key_len, block_mask, stream, dtype);
+                    key_len, block_mask, stream, dtype, workspace, workspace_bytes);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int H_kv, int N, int d) {
+    if ((d != 64 && d != 128) || B < 1 || H < 1 || H_kv < 1 || N < 1 || H % H_kv != 0) return 0;
+    return (size_t)fa::bwd_workspace_bytes(B, H, H_kv, N, d);
 }
 
 int fa_tile_shape(int dtype, int d, int block_sparse, int Br, int Bc, int *br_out, int *bc_out) {

@@ -154,6 +154,44 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
+// Workgroup -> (query-head split, batch * key/value head, key block).  The
+// blockIdx is first renumbered so that each XCD gets a contiguous run; the
+// splits of one key block are adjacent (they read the same K and V), and
+// within a head the key blocks run in ascending order (causal: the ones that
+// see the most query rows first).
+__device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt) {
+    int id = blockIdx.x;
+    const int G = gridDim.x;
+    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
+    *split = id % nsplit;
+    id /= nsplit;
+    *bkv = id / nkt;
+    *kt = id - *bkv * nkt;
+}
+
+// Sum of the nsplit fp32 partials of dK (times the scale) and dV, rounded
+// once to the element type.  Four consecutive elements per thread, in split
+// order (deterministic).
+template <class T>
+__global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a, int64_t el) {
+    using x4_t = typename Elem<T>::x4;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= el) return;
+    f32x4_t sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.nsplit; ++s) {
+        sk += *reinterpret_cast<const f32x4_t *>(a.part + (int64_t)(2 * s) * el + i);
+        sv += *reinterpret_cast<const f32x4_t *>(a.part + (int64_t)(2 * s + 1) * el + i);
+    }
+    x4_t wk, wv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        wk[j] = (T)(sk[j] * a.scale);
+        wv[j] = (T)sv[j];
+    }
+    *reinterpret_cast<x4_t *>(reinterpret_cast<T *>(a.dk) + i) = wk;
+    *reinterpret_cast<x4_t *>(reinterpret_cast<T *>(a.dv) + i) = wv;
+}
+
 template <class T, int D, int NW, int QT, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     using x8_t = typename Elem<T>::x8;
@@ -171,13 +209,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = a.N;
     const int nkt = (N + BK - 1) / BK;
-    // Workgroup -> (batch, key/value head, key block); causal grids start
-    // with the key blocks that see the most query rows.
-    int id = blockIdx.x;
-    const int G = gridDim.x;
-    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
-    const int bkv = id / nkt;
-    int kt = id - bkv * nkt;
+    // Workgroup -> (batch, key/value head, key block, query-head split);
+    // causal grids start with the key blocks that see the most query rows.
+    int split, bkv, kt;
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + wave * 32;
@@ -218,11 +253,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     const int qt_first = CAUSAL ? k0 / BQ : 0;
     const int nqt = (N + BQ - 1) / BQ;
     const int steps_per_head = nqt - qt_first;
+    // This workgroup's query heads: group / nsplit of the group.
+    const int gsplit = a.group / a.nsplit;
     // workgroup-uniform (every wave takes part in the copies and barriers)
-    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * a.group;
+    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * gsplit;
     auto step_tile = [&](int s, int *hq, int *qt) {
         const int g = s / steps_per_head;
-        *hq = b * a.H + hkv * a.group + g;
+        *hq = b * a.H + hkv * a.group + split * gsplit + g;
         *qt = qt_first + (s - g * steps_per_head);
     };
     auto tile_active = [&](int qt) {
@@ -332,8 +369,26 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     }
 
     // dK = scale * (dK^T)^T, dV: lane holds key lane % 32, head dims
-    // 32*mb + 8*gg + 4*(lane/32) .. +3.
-    if (key < N) {
+    // 32*mb + 8*gg + 4*(lane/32) .. +3.  With a query-head split, fp32
+    // partials (dK before the scale) go to the workspace instead.
+    if (key < N && a.nsplit > 1) {
+        const int64_t el = (int64_t)a.B * a.Hkv * N * D;
+        float *pk = a.part + (int64_t)(2 * split) * el + kvhead + (int64_t)key * D;
+        float *pv = pk + el;
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                f32x4_t wk, wv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    wk[j] = dk[mb][4 * gg + j];
+                    wv[j] = dv[mb][4 * gg + j];
+                }
+                *reinterpret_cast<f32x4_t *>(pk + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
+                *reinterpret_cast<f32x4_t *>(pv + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
+            }
+    } else if (key < N) {
         const float scale = a.scale;
         T *dK = reinterpret_cast<T *>(a.dk) + kvhead + (int64_t)key * D;
         T *dV = reinterpret_cast<T *>(a.dv) + kvhead + (int64_t)key * D;
@@ -380,11 +435,8 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     const int kg = wave & 3, qh = wave >> 2;
     const int N = a.N;
     const int nkt = (N + BK - 1) / BK;
-    int id = blockIdx.x;
-    const int G = gridDim.x;
-    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
-    const int bkv = id / nkt;
-    const int kt = id - bkv * nkt;
+    int split, bkv, kt;
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + kg * 32;
@@ -412,10 +464,11 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     const int qt_first = CAUSAL ? k0 / BQ : 0;
     const int nqt = (N + BQ - 1) / BQ;
     const int steps_per_head = nqt - qt_first;
-    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * a.group;
+    const int gsplit = a.group / a.nsplit;
+    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * gsplit;
     auto step_tile = [&](int s, int *hq, int *qt) {
         const int g = s / steps_per_head;
-        *hq = b * a.H + hkv * a.group + g;
+        *hq = b * a.H + hkv * a.group + split * gsplit + g;
         *qt = qt_first + (s - g * steps_per_head);
     };
     auto tile_active = [&](int qt) {
@@ -539,7 +592,27 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
             }
     }
     __syncthreads();
-    if (qh == 0 && key < N) {
+    if (qh == 0 && key < N && a.nsplit > 1) {
+        // fp32 partials of this query-head split (dK before the scale)
+        const int64_t el = (int64_t)a.B * a.Hkv * N * D;
+        float *pk = a.part + (int64_t)(2 * split) * el + kvhead + (int64_t)key * D;
+        float *pv = pk + el;
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const f32x4_t xk = red[((2 * mb) * 4 + gg) * 64 + lane];
+                const f32x4_t xv = red[((2 * mb + 1) * 4 + gg) * 64 + lane];
+                f32x4_t wk, wv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    wk[j] = dk[mb][4 * gg + j] + xk[j];
+                    wv[j] = dv[mb][4 * gg + j] + xv[j];
+                }
+                *reinterpret_cast<f32x4_t *>(pk + mb * 32 + 8 * gg + 4 * (lane / 32)) = wk;
+                *reinterpret_cast<f32x4_t *>(pv + mb * 32 + 8 * gg + 4 * (lane / 32)) = wv;
+            }
+    } else if (qh == 0 && key < N) {
         const float scale = a.scale;
         T *dK = reinterpret_cast<T *>(a.dk) + kvhead + (int64_t)key * D;
         T *dV = reinterpret_cast<T *>(a.dv) + kvhead + (int64_t)key * D;
@@ -718,14 +791,19 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     // bwd_dkdv (d = 64 without the causal mask): 64 query rows per step, two
     // workgroups per CU (128 rows would spill)
     constexpr int QT = 2;
+    const unsigned kgrid = (unsigned)(nkt * a.B * a.Hkv * a.nsplit);
     if constexpr (D == 128 || CAUSAL)
-        hipLaunchKernelGGL((bwd_dkdv_pair<T, D, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0, stream,
-                           a);
+        hipLaunchKernelGGL((bwd_dkdv_pair<T, D, CAUSAL>), dim3(kgrid), dim3(512), 0, stream, a);
     else
-        hipLaunchKernelGGL((bwd_dkdv<T, D, NW, QT, CAUSAL>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(NW * 64),
-                           0, stream, a);
+        hipLaunchKernelGGL((bwd_dkdv<T, D, NW, QT, CAUSAL>), dim3(kgrid), dim3(NW * 64), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.nsplit > 1) {
+        const int64_t el = (int64_t)a.B * a.Hkv * a.N * D;
+        hipLaunchKernelGGL((bwd_reduce<T>), dim3((unsigned)((el / 4 + 255) / 256)), dim3(256), 0, stream, a, el);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
     constexpr int KT = 2;
     hipLaunchKernelGGL((bwd_dq<T, D, NW, KT, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream,
@@ -741,6 +819,29 @@ hipError_t launch_bwd_typed(const BwdArgs &a, int d, int causal, hipStream_t str
 }
 
 }  // namespace
+
+// A query-head split pays when the dK/dV grid (one workgroup per key/value
+// head and 128-key block, one workgroup per CU) is small: if the unsplit
+// grid has fewer than 512 workgroups, the largest divisor of the group that
+// keeps the grid within 2048.  (Measured: splitting a grid that already has
+// 512 made the backward slower; multi-query at 16K gained 1.6x at 1024
+// workgroups and 5 % more at 2048.)
+int bwd_split(int B, int H, int Hkv, int N) {
+    if (B < 1 || H < 1 || Hkv < 1 || N < 1 || H % Hkv != 0) return 1;
+    const int64_t base = (int64_t)B * Hkv * ((N + 127) / 128);
+    const int group = H / Hkv;
+    if (group == 1 || base >= 512) return 1;
+    int best = 1;
+    for (int s = 2; s <= group; ++s)
+        if (group % s == 0 && base * s <= 2048) best = s;
+    return best;
+}
+
+uint64_t bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+    const int s = bwd_split(B, H, Hkv, N);
+    if (s == 1) return 0;
+    return (uint64_t)s * 2 * (uint64_t)B * Hkv * (uint64_t)N * d * sizeof(float);
+}
 
 hipError_t launch_bwd(const BwdArgs &a, int d, int causal, int f16, hipStream_t stream) {
     return f16 ? launch_bwd_typed<_Float16>(a, d, causal, stream) : launch_bwd_typed<__bf16>(a, d, causal, stream);

@@ -27,10 +27,10 @@ struct FwdArgs {
 
 // Everything the backward kernels need.
 struct BwdArgs {
-    const void *q, *k, *v, *o, *dout;  // bf16 [B,H,N,d] (k, v: [B,Hkv,N,d])
+    const void *q, *k, *v, *o, *dout;  // bf16 or fp16 [B,H,N,d] (k, v: [B,Hkv,N,d])
     const float *lse;                  // [B,H,N], natural log, from the forward
     float *delta;                      // [B,H,N] workspace: dO_i . O_i
-    void *dq, *dk, *dv;                // bf16 outputs (dk, dv: [B,Hkv,N,d])
+    void *dq, *dk, *dv;                // outputs (dk, dv: [B,Hkv,N,d])
     const int32_t *key_len;
     const uint8_t *block_mask;
     int B, H, N;
@@ -38,9 +38,20 @@ struct BwdArgs {
     int nkb;
     float scale;       // softmax scale
     float scale_log2;  // scale * log2(e)
+    // Query-head split of each key/value head's group: nsplit workgroups per
+    // key block each take group / nsplit query heads and write fp32 partial
+    // dK (before the scale) and dV to part ([nsplit][2][B*Hkv*N*d], dK then
+    // dV); a reduce kernel adds them.  nsplit = 1: no split, part unused.
+    int nsplit;
+    float *part;
 };
 
-// Enqueues the three backward kernels on `stream`.
+// Query-head split the backward uses for a shape when given a workspace, and
+// the workspace bytes it then needs (0 when no split is worth it).
+int bwd_split(int B, int H, int Hkv, int N);
+uint64_t bwd_workspace_bytes(int B, int H, int Hkv, int N, int d);
+
+// Enqueues the backward kernels on `stream`.
 hipError_t launch_bwd(const BwdArgs &a, int d, int causal, int f16, hipStream_t stream);
 
 // Enqueues one forward pass on `stream`; returns the launch status.

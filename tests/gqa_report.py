@@ -8,8 +8,9 @@ key/value heads.  This report runs the 16K causal shape (B1 H16 N16384 d128,
 band + global 128x128 mask) with H_kv = 16 (multi-head), 4 (groups of four)
 and 1 (multi-query).  Per point: forward and backward time per call (HIP
 events on the launch stream, 10 timed calls after 3 warm-up calls), TFLOP/s
-(forward 4*d, backward 10*d per visible pair), and max|dO| / max|dLSE| of
-the forward on 32 seeded rows against the FP64 oracle.
+(forward 4*d, backward 10*d per visible pair), the backward also without
+its split workspace, and max|dO| / max|dLSE| of the forward on 32 seeded
+rows against the FP64 oracle.
 
     python tests/gqa_report.py [--json PATH]
 """
@@ -48,8 +49,9 @@ def main():
     ap.add_argument("--reps", type=int, default=10)
     args = ap.parse_args()
     rows = []
-    print("| shape | H_kv | fwd us | fwd TFLOP/s | bwd us | bwd TFLOP/s | max abs dO | max abs dLSE |")
-    print("|---|---|---|---|---|---|---|---|", flush=True)
+    print("| shape | H_kv | fwd us | fwd TFLOP/s | bwd us | bwd TFLOP/s | bwd us, no workspace | workspace MiB "
+          "| max abs dO | max abs dLSE |")
+    print("|---|---|---|---|---|---|---|---|---|---|", flush=True)
     for key in ("long_causal", "block_sparse"):
         w = WORKLOADS[key]
         B, H, N, d = w.B, w.H, w.N, w.d
@@ -70,9 +72,14 @@ def main():
             delta = torch.empty_like(lse)
             fwd_us = timed(lambda: fa.fwd(tq, tk, tv, causal=w.causal, block_mask=tbm, scale=scale,
                                           out=o, lse=lse), args.reps)
+            need = fa.fa_bwd_workspace_size(B, H, hkv, N, d)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
             bwd_us = timed(lambda: fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, block_mask=tbm,
                                           scale=scale, dq=grads[0], dk=grads[1], dv=grads[2],
-                                          delta=delta), args.reps)
+                                          delta=delta, workspace=ws), args.reps)
+            bwd_plain_us = timed(lambda: fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, block_mask=tbm,
+                                                scale=scale, dq=grads[0], dk=grads[1], dv=grads[2],
+                                                delta=delta, workspace=None), args.reps)
             pairs = allowed_pairs(N, B, H, w.causal, None, bm)
             sample = np.sort(rng.choice(B * H * N, size=32, replace=False))
             o_ref, l_ref = oracle.attention_rows_f64(q, k, v, sample, scale, w.causal, None, bm)
@@ -81,11 +88,12 @@ def main():
             d_l = float(np.abs(lse.reshape(-1)[idx].double().cpu().numpy() - l_ref).max())
             r = dict(shape=key, H_kv=hkv, fwd_us=fwd_us, fwd_tflops=4 * d * pairs / (fwd_us * 1e-6) / 1e12,
                      bwd_us=bwd_us, bwd_tflops=10 * d * pairs / (bwd_us * 1e-6) / 1e12,
-                     max_dO=d_o, max_dLSE=d_l)
+                     bwd_no_workspace_us=bwd_plain_us, workspace_bytes=need, max_dO=d_o, max_dLSE=d_l)
             rows.append(r)
             print(f"| {key} | {hkv} | {fwd_us:.1f} | {r['fwd_tflops']:.1f} | {bwd_us:.1f} | "
-                  f"{r['bwd_tflops']:.1f} | {d_o:.2e} | {d_l:.2e} |", flush=True)
-            del tq, tk, tv, tdo, o, lse, grads, delta
+                  f"{r['bwd_tflops']:.1f} | {bwd_plain_us:.1f} | {need / 2**20:.0f} | {d_o:.2e} | {d_l:.2e} |",
+                  flush=True)
+            del tq, tk, tv, tdo, o, lse, grads, delta, ws
     if args.json:
         with open(args.json, "w") as f:
             json.dump(rows, f, indent=1)

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study",
-                                           "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "fa_tile_shape",
+                                           "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_tile_shape",
                                            "fa_status_string", "fa_last_hip_error"])
 
 
@@ -138,7 +138,7 @@ def test_bwd_invalid_arguments_return_status_without_launch(kw, status, entry):
     if entry == "fa_bwd":
         rc = lib.fa_bwd(*[args[n] for n in names])
     else:
-        rc = lib.fa_bwd_ex(*[args[n] for n in names], fa.DTYPE_F16)
+        rc = lib.fa_bwd_ex(*[args[n] for n in names], fa.DTYPE_F16, None, 0)
     assert rc == status
 
 
@@ -146,8 +146,43 @@ def test_bwd_invalid_arguments_return_status_without_launch(kw, status, entry):
 def test_bwd_ex_rejects_unbuilt_dtypes(dtype):
     lib = fa._load()
     rc = lib.fa_bwd_ex(Q, K, V, O, DO, LSEB, DELTA, DQ, DK, DV, 2, 4, 2, 100, 64, 0.125, 0, None, None,
-                       None, dtype)
+                       None, dtype, None, 0)
     assert rc == 5
+
+
+WS = 0x78000000
+
+
+@pytest.mark.parametrize("ws,nbytes,status", [
+    (WS, 409600 - 1, 7),        # smaller than fa_bwd_workspace_size
+    (WS + 8, 409600, 7),        # not 16-byte aligned
+    (DQ + 64, 409600, 7),       # over an output
+    (Q, 409600, 7),             # over an input
+])
+def test_bwd_workspace_validation(ws, nbytes, status):
+    # B2 H4 H_kv2 N100 d64: grouped heads on a tiny grid, so a split is used
+    assert fa.fa_bwd_workspace_size(2, 4, 2, 100, 64) == 409600
+    lib = fa._load()
+    rc = lib.fa_bwd_ex(Q, K, V, O, DO, LSEB, DELTA, DQ, DK, DV, 2, 4, 2, 100, 64, 0.125, 0, None, None,
+                       None, fa.DTYPE_BF16, ws, nbytes)
+    assert rc == status
+
+
+def test_bwd_workspace_size():
+    size = fa.fa_bwd_workspace_size
+    # plain multi-head attention never splits
+    assert size(1, 16, 16, 16384, 128) == 0 and size(8, 12, 12, 1024, 64) == 0
+    # multi-query 16K: 128 key blocks; the largest divisor of 16 keeping the
+    # grid within 2048 workgroups is 16 -> 16 splits x (dK, dV) x N x d floats
+    assert size(1, 16, 1, 16384, 128) == 16 * 2 * 16384 * 128 * 4
+    # four key/value heads at 16K already give 512 workgroups: no split
+    assert size(1, 16, 4, 16384, 128) == 0
+    # 8 query heads per key/value head, 2 x 32 key blocks = 64 -> 8 splits
+    assert size(2, 16, 2, 4096, 64) == 8 * 2 * 2 * 2 * 4096 * 64 * 4
+    # 12 query heads per key/value head on 1 x 100 key blocks -> 12 splits
+    assert size(1, 12, 1, 12800, 64) == 12 * 2 * 12800 * 64 * 4
+    # invalid shapes report 0
+    assert size(0, 4, 2, 100, 64) == 0 and size(1, 4, 3, 100, 64) == 0 and size(1, 4, 2, 100, 96) == 0
 
 
 def test_status_strings_cover_every_code():

@@ -40,7 +40,7 @@ def dev(x, dtype="bf16"):
 
 
 def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None, scale=None,
-             dtype="bf16"):
+             dtype="bf16", workspace=True):
     q, _, _, rng = random_qkv(B, H, N, d, seed, dtype)
     _, k, v, rng = random_qkv(B, H_kv, N, d, seed + 1, dtype, rng=rng)
     dout = rng.standard_normal(q.shape).astype(np.float32)
@@ -54,7 +54,7 @@ def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None
     dk = torch.full_like(tk, float("nan"))
     dv = torch.full_like(tv, float("nan"))
     fa.bwd(tq, tk, tv, o, tdo, lse, causal=causal, key_len=kl, block_mask=bm, scale=float(scale),
-           dq=dq, dk=dk, dv=dv)
+           dq=dq, dk=dk, dv=dv, workspace=workspace)
     torch.cuda.synchronize()
     ref = oracle.attention_bwd_f64(q, k, v, dout_b, float(scale), causal,
                                    None if key_len is None else np.asarray(key_len, dtype=np.int32),
@@ -102,16 +102,44 @@ def test_bwd_f16_grouped_heads(causal):
     run_case(1, 8, 2, 257, 128, seed=92, causal=causal, dtype="f16")
 
 
+# Grouped heads on these small grids take the query-head split (fp32 partial
+# dK, dV in a workspace, summed by a second kernel) unless no workspace is
+# given; both paths are checked.
+@pytest.mark.parametrize("split", [True, None])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("H,H_kv", [(8, 2), (4, 1)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_grouped_heads(d, H, H_kv, causal):
-    run_case(1, H, H_kv, 200, d, seed=72, causal=causal)
+def test_bwd_grouped_heads(split, d, H, H_kv, causal):
+    assert fa.fa_bwd_workspace_size(1, H, H_kv, 200, d) > 0
+    run_case(1, H, H_kv, 200, d, seed=72, causal=causal, workspace=split)
 
 
+@pytest.mark.parametrize("split", [True, None])
 @pytest.mark.parametrize("mode", ["padded", "blocks", "all"])
-def test_bwd_grouped_heads_masked(mode):
-    run_case(2, 6, 2, 300, 64, seed=77, **modes(300, 78)[mode])
+def test_bwd_grouped_heads_masked(split, mode):
+    run_case(2, 6, 2, 300, 64, seed=77, workspace=split, **modes(300, 78)[mode])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_split_f16_and_stale_workspace(d):
+    # fp16 through the split path, with a workspace full of garbage on entry
+    need = fa.fa_bwd_workspace_size(2, 12, 3, 333, d)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    run_case(2, 12, 3, 333, d, seed=79, causal=True, dtype="f16", workspace=ws)
+
+
+def test_bwd_split_deterministic():
+    q, k, v, rng = random_qkv(1, 8, 300, 64, 80, "bf16")
+    k, v = k[:, :1].copy(), v[:, :1].copy()
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    tdo = dev(rng.standard_normal(q.shape).astype(np.float32))
+    o, lse = fa.fwd(tq, tk, tv, causal=True)
+    a = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True)
+    b = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 @pytest.mark.parametrize("workload", ["gpt2_causal", "bert_padded", "long_causal", "block_sparse"])
@@ -208,3 +236,37 @@ def test_gqa_full_size_sampled():
         err = float(np.abs(g - r).max())
         bound = TOL_REL * max(1.0, float(np.abs(r).max()))
         assert err <= bound, f"GQA {name}: max|dg| = {err:.3e} > {bound:.3e}"
+
+
+
+def test_mqa_block_sparse_full_size_sampled():
+    # Multi-query attention at the block-sparse shape (B4 H16 N4096 d64, one
+    # key/value head, the band + global mask): the backward splits each key
+    # block's 16 query heads over 8 workgroups.  dQ on sampled rows, dK and
+    # dV on sampled keys against the oracle summed over all 16 query heads.
+    w = WORKLOADS["block_sparse"]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    rng = np.random.Generator(np.random.PCG64(3105))
+    q = random_qkv(B, H, N, d, 0, "bf16", rng=rng)[0]
+    _, k, v, rng = random_qkv(B, 1, N, d, 0, "bf16", rng=rng)
+    bm = band_global_block_mask((N + 127) // 128, rng, w.sparse_globals)
+    assert fa.fa_bwd_workspace_size(B, H, 1, N, d) > 0
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    tdo = dev(rng.standard_normal(q.shape, dtype=np.float32))
+    tbm = torch.from_numpy(bm).cuda()
+    o, lse = fa.fwd(tq, tk, tv, block_mask=tbm, scale=scale)
+    dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, block_mask=tbm, scale=scale)
+    torch.cuda.synchronize()
+    rows = rng.choice(B * H * N, size=24, replace=False)
+    cols = int(rng.integers(B)) * N + np.unique(np.concatenate([[0, N - 1], rng.choice(N, 10)]))
+    dout = tdo.float().cpu().numpy()
+    ref = {"dq": oracle.attention_bwd_rows_f64(q, k, v, dout, rows, scale, False, None, bm)}
+    ref["dk"], ref["dv"] = oracle.attention_bwd_cols_f64(q, k, v, dout, cols, scale, False, None, bm)
+    rows_t, cols_t = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    got = {"dq": dq.reshape(-1, d)[rows_t], "dk": dk.reshape(-1, d)[cols_t], "dv": dv.reshape(-1, d)[cols_t]}
+    for name, r in ref.items():
+        g = got[name].double().cpu().numpy()
+        err = float(np.abs(g - r).max())
+        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        assert err <= bound, f"MQA {name}: max|dg| = {err:.3e} > {bound:.3e}"
