@@ -154,15 +154,13 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
-// Workgroup -> (query-head split, batch * key/value head, key block).  The
-// blockIdx is first renumbered so that each XCD gets a contiguous run; the
-// splits of one key block are adjacent (they read the same K and V), and
-// within a head the key blocks run in ascending order (causal: the ones that
-// see the most query rows first).
+// Workgroup -> (query-head split, batch * key/value head, key block), via
+// the XCD-aware item order of xcd_item: the splits of one key block are
+// adjacent (they read the same K and V), and within a head the key blocks
+// run in ascending order (causal: the ones that see the most query rows
+// first).
 __device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt) {
-    int id = blockIdx.x;
-    const int G = gridDim.x;
-    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
+    int id = xcd_item(nkt * nsplit);
     *split = id % nsplit;
     id /= nsplit;
     *bkv = id / nkt;

@@ -79,11 +79,31 @@ __device__ __forceinline__ int kv_head_of(int bh, const Args &a) {
 // receives one contiguous run of logical tiles (whole heads where possible),
 // keeping a head's K/V re-reads inside one XCD's L2.  Causal grids visit the
 // longest query tiles of a head first.
+// Work item of this workgroup.  The grid's items come in runs of per_head
+// (one head's tiles, heaviest first when the mask is causal).  Workgroups
+// are handed to the 8 XCDs round-robin (blockIdx % 8), and each XCD has its
+// own L2, so each XCD gets a contiguous share of the items: whole heads
+// when a head fits in one share, so that a head's K/V (or Q/dO) stays in one
+// L2.  When a head's run spans X XCDs, those X XCDs take its items
+// round-robin instead of X contiguous pieces, so that each gets heavy and
+// light tiles alike; contiguous pieces would hand one XCD all the long
+// causal rows.
+__device__ __forceinline__ int xcd_item(int per_head) {
+    const int G = gridDim.x;
+    const int id = blockIdx.x;
+    if ((G & 7) != 0) return id;
+    const int per = G >> 3, x = id & 7, local = id >> 3;
+    if (per_head > per && per_head % per == 0) {
+        const int X = per_head / per;  // XCDs per head; G = (8 / X) heads * per_head
+        const int head = x / X, j = x - head * X;
+        return head * per_head + j + X * local;
+    }
+    return x * per + local;
+}
+
 __device__ __forceinline__ void tile_of_block(int nqt, bool longest_first,
                                               int *bh, int *qt) {
-    const int G = gridDim.x;
-    int id = blockIdx.x;
-    if ((G & 7) == 0) id = (id & 7) * (G >> 3) + (id >> 3);
+    const int id = xcd_item(nqt);
     *bh = id / nqt;
     const int r = id - *bh * nqt;
     *qt = longest_first ? nqt - 1 - r : r;

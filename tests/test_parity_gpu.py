@@ -192,6 +192,15 @@ def test_very_long_sequences_sampled_rows(N, d, causal):
               f"N={N} tile study")
 
 
+@pytest.mark.parametrize("H,N,Br", [(2, 4096, 0), (1, 4096, 0), (4, 4096, 64), (2, 4096, 32)])
+def test_heads_spanning_several_xcds(H, N, Br):
+    """Few heads: one head's query tiles are shared round-robin by several
+    XCDs (2, 4 or 8 per head); every output against the oracle."""
+    inp = custom(1, H, N, 128, seed=95 + H, causal=True, amp=0.5)
+    o, lse = run(inp, Br=Br, Bc=64 if Br else 0)
+    check(o, lse, *ref(inp), TOL_BF16, f"H={H} N={N} Br={Br}")
+
+
 @pytest.mark.parametrize("Br", [16, 32, 64, 128])
 @pytest.mark.parametrize("Bc", [16, 32, 64, 128])
 def test_tile_sweep_slice(Br, Bc):
