@@ -169,6 +169,36 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
                hipStream_t stream, int dtype, int Br, int Bc);
 
 /*
+ * Forward with a key-range split for grids too small to fill the GPU (few
+ * heads, e.g. one GPU's share of a head-sharded problem): each query tile's
+ * key tiles are shared out over several workgroups, each writing an fp32
+ * partial O (normalised by its own row sum) and partial log-sum-exp to the
+ * workspace, and a second kernel merges them per row,
+ *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
+ * the same combination that merges results computed on different key
+ * ranges anywhere.  Same arguments as fa_fwd_gqa with the tuned tile, plus
+ *   dtype     : FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32 runs unsplit)
+ *   workspace : DEVICE memory owned by the caller (16-byte aligned) of
+ *               workspace_bytes bytes, or NULL.  fa_fwd_workspace_size
+ *               gives the bytes needed; when it is 0, or workspace is NULL,
+ *               the call is fa_fwd_gqa with Br = Bc = 0.  A non-NULL
+ *               workspace smaller than needed, misaligned, or overlapping an
+ *               input or output: FA_ERR_INVALID_ARG.  Its contents on entry
+ *               do not matter; every byte the split uses is written first.
+ * The result equals the unsplit one up to rounding (the shares' rows are
+ * combined in fp32 and rounded to the output type once).
+ */
+int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int H_kv, int N, int d, float scale, int causal,
+              const int32_t *key_len, const uint8_t *block_mask,
+              hipStream_t stream, int dtype, void *workspace,
+              size_t workspace_bytes);
+
+/* Workspace bytes fa_fwd_ws uses for this shape and dtype (0: none is used,
+ * or the arguments are invalid).  Independent of H_kv, masks and scale. */
+size_t fa_fwd_workspace_size(int B, int H, int N, int d, int dtype);
+
+/*
  * Backward pass: the gradients of the loss sum(dout * o) with respect to q,
  * k and v, for bf16 attention computed by fa_fwd / fa_fwd_gqa with the same
  * scale, causal flag, key_len and block_mask.  The pages give only the

@@ -1,8 +1,8 @@
 """Python binding of the gfx950 exact-attention library (libfa.so).
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
-``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_bwd``, ``fa_bwd_ex``,
-``fa_bwd_workspace_size``, ``fa_tile_shape``,
+``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_fwd_ws``, ``fa_fwd_workspace_size``,
+``fa_bwd``, ``fa_bwd_ex``, ``fa_bwd_workspace_size``, ``fa_tile_shape``,
 ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
@@ -14,7 +14,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "bwd",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size", "fa_bwd", "fa_bwd_ex",
+           "fa_bwd_workspace_size", "bwd",
            "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING", "ORDER_SHUFFLED",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
            "DTYPE_BF16", "DTYPE_F32", "DTYPE_F16", "MASK_BLOCK"]
@@ -77,6 +78,11 @@ def _load():
     lib.fa_bwd_ex.restype = i32
     lib.fa_bwd_workspace_size.argtypes = [i32] * 5
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_ws.argtypes = [vp] * 5 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp, i32, vp,
+                                                     ctypes.c_size_t]
+    lib.fa_fwd_ws.restype = i32
+    lib.fa_fwd_workspace_size.argtypes = [i32] * 5
+    lib.fa_fwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fa_tile_shape.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -139,6 +145,16 @@ def fa_bwd_ex(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale,
                              workspace_bytes), "fa_bwd_ex")
 
 
+def fa_fwd_ws(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream, dtype,
+              workspace, workspace_bytes):
+    _check(_load().fa_fwd_ws(q, k, v, o, lse, B, H, H_kv, N, d, scale, int(bool(causal)), key_len,
+                             block_mask, stream, dtype, workspace, workspace_bytes), "fa_fwd_ws")
+
+
+def fa_fwd_workspace_size(B, H, N, d, dtype):
+    return int(_load().fa_fwd_workspace_size(B, H, N, d, dtype))
+
+
 def fa_bwd_workspace_size(B, H, H_kv, N, d):
     return int(_load().fa_bwd_workspace_size(B, H, H_kv, N, d))
 
@@ -162,7 +178,7 @@ def fa_last_hip_error():
 
 
 def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, Bc=0,
-        out=None, lse=None, stream=None, tile_order=ORDER_ASCENDING):
+        out=None, lse=None, stream=None, tile_order=ORDER_ASCENDING, workspace=None):
     """Attention forward on device tensors.
 
     q: contiguous [B, H, N, d] cuda tensor, bfloat16, float16 or float32; k, v: the
@@ -174,7 +190,10 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
     q and lse float32 [B, H, N]; `out`/`lse` may be passed preallocated, and
     lse=False skips the logsumexp (returned as None).  tile_order =
     ORDER_DESCENDING visits key tiles last-first, ORDER_SHUFFLED in a fixed
-    permutation (tile-study kernels only).
+    permutation (tile-study kernels only).  ``workspace`` (tuned tile only):
+    True allocates the key-range split workspace ``fa_fwd_workspace_size``
+    asks for (grids too small for the GPU), a uint8 cuda tensor is used as
+    it, None (the default) runs unsplit.
     """
     import torch
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -214,7 +233,18 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
         bm_ptr = block_mask.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    if tile_order != ORDER_ASCENDING:
+    if workspace is not None and workspace is not False:
+        if tile_order != ORDER_ASCENDING or Br or Bc:
+            raise ValueError("the split workspace applies to the tuned tile in ascending order")
+        if workspace is True:
+            need = fa_fwd_workspace_size(B, H, N, d, dtype)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 cuda tensor")
+        fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                  lse.data_ptr() if want_lse else None, B, H, H_kv, N, d, float(scale),
+                  causal, kl_ptr, bm_ptr, stream, dtype, workspace.data_ptr(), workspace.numel())
+    elif tile_order != ORDER_ASCENDING:
         if H_kv != H:
             raise ValueError("tile_order applies to plain multi-head calls only")
         fa_fwd_study(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -62,7 +62,7 @@ int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
 int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
             int Hkv, int N, int d, float scale, int causal, const int32_t *key_len,
             const uint8_t *block_mask, hipStream_t stream, int dtype, int br, int bc,
-            int order = FA_ORDER_ASCENDING) {
+            int order = FA_ORDER_ASCENDING, void *workspace = nullptr, size_t workspace_bytes = 0) {
     if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
     if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -92,6 +92,17 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
                                 &tbc, &study);
     if (rc != FA_OK) return rc;
     if (order != FA_ORDER_ASCENDING && !study) return FA_ERR_UNSUPPORTED_TILE;
+    // Key-range split (fa_fwd_ws): used when a workspace is given and the
+    // shape gains from it; bf16/fp16 with the tuned tile only.
+    const uint64_t need = fa::fwd_workspace_bytes(B, H, N, d);
+    const bool split = workspace && need > 0 && dtype != FA_DTYPE_F32;
+    if (split) {
+        if (workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
+        if (overlaps(workspace, need, q, bytes) || overlaps(workspace, need, k, kv_bytes) ||
+            overlaps(workspace, need, v, kv_bytes) || overlaps(workspace, need, o, bytes) ||
+            (lse && overlaps(workspace, need, lse, lse_bytes)))
+            return FA_ERR_INVALID_ARG;
+    }
 
     fa::FwdArgs a;
     a.q = q;
@@ -109,8 +120,13 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     a.nkb = (N + 127) / 128;
     a.order = order;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.nsplit = split ? fa::fwd_split(B, H, N) : 1;
+    const uint64_t rows = (uint64_t)B * H * N;
+    a.part_o = split ? static_cast<float *>(workspace) : nullptr;
+    a.part_l = split ? static_cast<float *>(workspace) + (uint64_t)a.nsplit * rows * d : nullptr;
 
-    const hipError_t err = inst->launch(a, stream);
+    const hipError_t err = split ? fa::launch_fwd_split(a, d, causal ? 1 : 0, dtype == FA_DTYPE_F16 ? 1 : 0, stream)
+                                 : inst->launch(a, stream);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return FA_ERR_HIP;
@@ -215,6 +231,20 @@ int fa_fwd_study(const void *q, const void *k, const void *v, void *o, float *ls
                  int tile_order) {
     return forward(q, k, v, o, lse, B, H, H, N, d, scale, causal, key_len, block_mask, stream,
                    dtype, Br, Bc, tile_order);
+}
+
+int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+              int H_kv, int N, int d, float scale, int causal, const int32_t *key_len,
+              const uint8_t *block_mask, hipStream_t stream, int dtype, void *workspace,
+              size_t workspace_bytes) {
+    return forward(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
+                   dtype, 0, 0, FA_ORDER_ASCENDING, workspace, workspace_bytes);
+}
+
+size_t fa_fwd_workspace_size(int B, int H, int N, int d, int dtype) {
+    if ((d != 64 && d != 128) || B < 1 || H < 1 || N < 1) return 0;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return 0;
+    return (size_t)fa::fwd_workspace_bytes(B, H, N, d);
 }
 
 int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,

@@ -86,7 +86,7 @@ struct ChunkPlan {
     }
 };
 
-template <class T, int D, int BC, int NSTAGE, int NW, bool CAUSAL>
+template <class T, int D, int BC, int NSTAGE, int NW, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) {
     using E = Elem<T>;
     using x8_t = typename E::x8;
@@ -124,8 +124,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = a.N;
     const int nqt = (N + BR - 1) / BR;
-    int bh, qt;
-    tile_of_block(nqt, CAUSAL, &bh, &qt);
+    int bh, qt, split = 0;
+    if constexpr (SPLIT) {
+        // (query tile, key-range share): the shares of one query tile are
+        // adjacent items; heads and tiles in the usual XCD-aware order.
+        const int item = xcd_item(nqt * a.nsplit);
+        split = item % a.nsplit;
+        const int rest = item / a.nsplit;
+        bh = rest / nqt;
+        const int r = rest - bh * nqt;
+        qt = CAUSAL ? nqt - 1 - r : r;
+    } else {
+        tile_of_block(nqt, CAUSAL, &bh, &qt);
+    }
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
@@ -141,10 +152,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     int kv_end = kv_len;
     if (CAUSAL) kv_end = min(kv_end, q0 + BR);
     const int ntiles = (kv_end + BC - 1) / BC;
+    // Key tiles [tbeg, tend) of this workgroup: all of them, or one share of
+    // a key-range split.
+    const int tbeg = SPLIT ? (int)((int64_t)ntiles * split / a.nsplit) : 0;
+    const int tend = SPLIT ? (int)((int64_t)ntiles * (split + 1) / a.nsplit) : ntiles;
     const int klast = kv_len - 1;
     // Tiles this wave computes form a prefix of the workgroup's sequence.
     const int wlast = wq0 >= N ? -1 : (CAUSAL ? (wq0 + QW - 1) / BC : ntiles);
-    auto active = [&](int t) { return t < ntiles && t <= wlast; };
+    auto active = [&](int t) { return t < tend && t <= wlast; };
 
     // Block-sparse skipping (only launched with BR = 128, where the
     // workgroup's rows are one query block): the mask row is scanned 64 key
@@ -398,15 +413,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     // i%NSTAGE and of V(T[i+P]) into V stage (i-1)%NSTAGE, both freed by the
     // previous iteration.
     int tq[P + 1];
-    tq[0] = next_tile(0);
+    tq[0] = next_tile(tbeg);
 #pragma unroll
     for (int j = 1; j <= P; ++j) tq[j] = next_tile(tq[j - 1] + 1);
 #pragma unroll
     for (int j = 0; j <= P; ++j)
-        if (tq[j] < ntiles) copy(K, kstage(j), koff, tq[j]);
+        if (tq[j] < tend) copy(K, kstage(j), koff, tq[j]);
 #pragma unroll
     for (int j = 0; j < P; ++j)
-        if (tq[j] < ntiles) copy(V, vstage(j), voff, tq[j]);
+        if (tq[j] < tend) copy(V, vstage(j), voff, tq[j]);
     wait_copies();
     __syncthreads();
     if (active(tq[0])) qk_plain(sA, kstage(0));
@@ -416,13 +431,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
         const int t_new = next_tile(tq[P] + 1);         // T[i+P+1]
         // Copies younger than those of K(T[i+1]) and V(T[i]) were issued in
         // the last P-1 iterations; they may stay in flight when complete.
-        if (P > 1 && tq[P] < ntiles)
+        if (P > 1 && tq[P] < tend)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * ROUNDS * (P - 1)) : "memory");
         else
             wait_copies();
         stage_barrier();
-        if (t_new < ntiles) copy(K, kstage(u), koff, t_new);
-        if (tq[P] < ntiles) copy(V, vstage((u + NSTAGE - 1) % NSTAGE), voff, tq[P]);
+        if (t_new < tend) copy(K, kstage(u), koff, t_new);
+        if (tq[P] < tend) copy(V, vstage((u + NSTAGE - 1) % NSTAGE), voff, tq[P]);
         if (active(tq[0])) step(tq[0], s, sn, kstage((u + 1) % NSTAGE), vstage(u));
 #pragma unroll
         for (int j = 0; j < P; ++j) tq[j] = tq[j + 1];
@@ -430,26 +445,49 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     };
 
     while (true) {
-        if (tq[0] >= ntiles) break;
+        if (tq[0] >= tend) break;
         iteration(IntTag<0>{}, sA, sB);
-        if (tq[0] >= ntiles) break;
+        if (tq[0] >= tend) break;
         iteration(IntTag<1 % NSTAGE>{}, sB, sA);
         if constexpr (NSTAGE % 2 == 1 || NSTAGE == 4) {
             // Unrolled to a multiple of both NSTAGE and 2 (score ping-pong).
-            if (tq[0] >= ntiles) break;
+            if (tq[0] >= tend) break;
             iteration(IntTag<2 % NSTAGE>{}, sA, sB);
-            if (tq[0] >= ntiles) break;
+            if (tq[0] >= tend) break;
             iteration(IntTag<3 % NSTAGE>{}, sB, sA);
             if constexpr (NSTAGE == 3) {
-                if (tq[0] >= ntiles) break;
+                if (tq[0] >= tend) break;
                 iteration(IntTag<4 % NSTAGE>{}, sA, sB);
-                if (tq[0] >= ntiles) break;
+                if (tq[0] >= tend) break;
                 iteration(IntTag<5 % NSTAGE>{}, sB, sA);
             }
         }
     }
 
-    // Epilogue: normalise, round to bf16 once, write O and LSE.
+    // Epilogue: normalise, round to bf16 once, write O and LSE.  A share of
+    // a key-range split writes its fp32 partial O (normalised by its own
+    // sum) and partial LSE instead; a share with no allowed key writes
+    // O = 0, LSE = -inf, which the merge gives weight 0.
+    if constexpr (SPLIT) {
+        const int qrow = wq0 + lane % 32;
+        const float l_tot = group_sum<32>(l);
+        if (qrow < N) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const int64_t prow = ((int64_t)split * a.B * a.H + bh) * N + qrow;
+            float *orow = a.part_o + prow * D;
+#pragma unroll
+            for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    f32x4_t w;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) w[j] = o[mb][4 * gg + j] * inv;
+                    *reinterpret_cast<f32x4_t *>(orow + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
+                }
+            if (lane < 32) a.part_l[prow] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : kNegInf;
+        }
+        return;
+    }
     {
         const int qrow = wq0 + lane % 32;
         const float l_tot = group_sum<32>(l);
@@ -480,6 +518,68 @@ hipError_t launch_pipe(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Merge of the nsplit partial results of each query row (the log-sum-exp
+// combination): LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s,
+// rounded once to the element type.  Shares with LSE_s = -inf carry weight
+// 0; a row with no allowed key in any share gets O = 0, LSE = -inf.  D/8
+// lanes per row, 8 elements each; shares added in order (deterministic).
+template <class T, int D>
+__global__ __launch_bounds__(256) void fwd_merge(FwdArgs a) {
+    using x8_t = typename Elem<T>::x8;
+    constexpr int LPR = D / 8;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+    const int part = threadIdx.x % LPR;
+    if (row >= rows) return;
+    float mx = kNegInf;
+    for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, a.part_l[(int64_t)s * rows + row]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float lse = kNegInf;
+    if (mx != kNegInf) {
+        float wsum = 0.f;
+        for (int s = 0; s < a.nsplit; ++s) {
+            const float w = __expf(a.part_l[(int64_t)s * rows + row] - mx);
+            wsum += w;
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(a.part_o + ((int64_t)s * rows + row) * D + part * 8);
+            const f32x4_t x0 = src[0], x1 = src[1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[j] = fmaf(w, x0[j], acc[j]);
+                acc[4 + j] = fmaf(w, x1[j], acc[4 + j]);
+            }
+        }
+        const float inv = 1.f / wsum;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= inv;
+        lse = mx + __logf(wsum);
+    }
+    x8_t w8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w8[j] = (T)acc[j];
+    *reinterpret_cast<x8_t *>(reinterpret_cast<T *>(a.o) + row * D + part * 8) = w8;
+    if (a.lse && part == 0) a.lse[row] = lse;
+}
+
+template <class T, int D, bool CAUSAL>
+hipError_t launch_split(const FwdArgs &a, hipStream_t stream) {
+    constexpr int NW = 4, BR = 32 * NW;
+    const int nqt = (a.N + BR - 1) / BR;
+    hipLaunchKernelGGL((fwd_pipe<T, D, 64, 2, NW, CAUSAL, true>),
+                       dim3((unsigned)(nqt * a.B * a.H * a.nsplit)), dim3(NW * 64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((fwd_merge<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_split_typed(const FwdArgs &a, int d, int causal, hipStream_t stream) {
+    if (d == 64) return causal ? launch_split<T, 64, true>(a, stream) : launch_split<T, 64, false>(a, stream);
+    return causal ? launch_split<T, 128, true>(a, stream) : launch_split<T, 128, false>(a, stream);
+}
+
 #define FA_PIPE(T, D, BC, NS, NW) \
     Instance{D, 0, 32 * NW, BC, &launch_pipe<T, D, BC, NS, NW, false>}, \
     Instance{D, 1, 32 * NW, BC, &launch_pipe<T, D, BC, NS, NW, true>}
@@ -504,6 +604,32 @@ const Instance *f16_tuned_instances() {
         Instance{0, 0, 0, 0, nullptr},
     };
     return table;
+}
+
+// A key-range split pays when the grid (B*H query tiles of 128 rows) is too
+// small for the 256 CUs and a causal grid's longest tile dominates: if it
+// has fewer than 512 workgroups, the largest power of two (at most 16) that
+// keeps it within 1024.  (Measured on B1 H2 N16384: 4 shares 172 us,
+// 8 shares 181 us, 16 shares 246 us, unsplit 299 us; a grid of 512 gained
+// nothing.)
+int fwd_split(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1) return 1;
+    const int64_t base = (int64_t)B * H * ((N + 127) / 128);
+    if (base >= 512) return 1;
+    int s = 1;
+    while (s < 16 && base * s * 2 <= 1024) s *= 2;
+    return s;
+}
+
+uint64_t fwd_workspace_bytes(int B, int H, int N, int d) {
+    const int s = fwd_split(B, H, N);
+    if (s == 1) return 0;
+    return (uint64_t)s * B * H * (uint64_t)N * (d + 1) * sizeof(float);
+}
+
+hipError_t launch_fwd_split(const FwdArgs &a, int d, int causal, int f16, hipStream_t stream) {
+    return f16 ? launch_split_typed<_Float16>(a, d, causal, stream)
+               : launch_split_typed<__bf16>(a, d, causal, stream);
 }
 
 void bf16_default_tile(int d, int block_sparse, int *br, int *bc) {

@@ -23,7 +23,23 @@ struct FwdArgs {
     int order;                  // key-tile visit order: 0 ascending, 1 descending, 2 shuffled
                                 // (tile-study kernels only)
     float scale_log2;           // softmax scale * log2(e), fp32
+    // Key-range split (fa_fwd_ws): nsplit workgroups per query tile, each
+    // over a contiguous share of its key tiles, writing fp32 partial O
+    // (normalised by its own row sum) to part_o [nsplit][B*H*N][d] and its
+    // natural-log partial LSE to part_l [nsplit][B*H*N]; a merge kernel
+    // combines them.  nsplit = 1: no split, part_o/part_l unused.
+    int nsplit;
+    float *part_o, *part_l;
 };
+
+// Key-range split the forward uses for a shape when given a workspace, and
+// the workspace bytes it then needs (0 when no split is worth it).
+int fwd_split(int B, int H, int N);
+uint64_t fwd_workspace_bytes(int B, int H, int N, int d);
+
+// Enqueues the split forward (tuned kernel with key ranges, then the merge)
+// for bf16 (f16 = 0) or fp16 (f16 = 1).
+hipError_t launch_fwd_split(const FwdArgs &a, int d, int causal, int f16, hipStream_t stream);
 
 // Everything the backward kernels need.
 struct BwdArgs {

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study",
-                                           "fa_fwd_gqa", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_size", "fa_tile_shape",
+                                           "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size", "fa_bwd", "fa_bwd_ex",
+                                           "fa_bwd_workspace_size", "fa_tile_shape",
                                            "fa_status_string", "fa_last_hip_error"])
 
 
@@ -226,3 +227,37 @@ def test_tile_table():
         fa.fa_tile_shape(fa.DTYPE_BF16, 128, True, 256, 64)
     with pytest.raises(fa.FaError):
         fa.fa_tile_shape(fa.DTYPE_BF16, 64, False, 16, 256)
+
+
+
+def test_fwd_workspace_size():
+    size = fa.fa_fwd_workspace_size
+    # enough workgroups already: no split (B*H*ceil(N/128) >= 512)
+    assert size(1, 16, 16384, 128, fa.DTYPE_BF16) == 0 and size(4, 16, 4096, 64, fa.DTYPE_BF16) == 0
+    # B1 H2 N16384: 256 query tiles -> 4 shares (1024 workgroups); O and LSE per share
+    assert size(1, 2, 16384, 128, fa.DTYPE_BF16) == 4 * 2 * 16384 * (128 + 1) * 4
+    assert size(1, 2, 16384, 128, fa.DTYPE_F16) == 4 * 2 * 16384 * (128 + 1) * 4
+    # 300 tiles -> 2 shares (600 <= 1024 < 1200); 1 tile -> 16 shares (the cap)
+    assert size(3, 1, 12800, 64, fa.DTYPE_BF16) == 2 * 3 * 12800 * 65 * 4
+    assert size(1, 1, 100, 64, fa.DTYPE_BF16) == 16 * 100 * 65 * 4
+    # fp32 is never split; invalid arguments report 0
+    assert size(1, 2, 16384, 128, fa.DTYPE_F32) == 0
+    assert size(0, 2, 100, 64, 0) == 0 and size(1, 2, 100, 96, 0) == 0
+
+
+FWS = 0x7A000000
+
+
+@pytest.mark.parametrize("ws,nbytes,status", [
+    (FWS, 2 * 3 * 100 * 65 * 4 * 16 - 4, 7),   # smaller than needed
+    (FWS + 4, 2 * 3 * 100 * 65 * 4 * 16, 7),   # not 16-byte aligned
+    (O + 32, 2 * 3 * 100 * 65 * 4 * 16, 7),    # over the output
+    (K, 2 * 3 * 100 * 65 * 4 * 16, 7),         # over an input
+])
+def test_fwd_workspace_validation(ws, nbytes, status):
+    # B2 H3 N100 d64: 6 query tiles -> 16 shares
+    assert fa.fa_fwd_workspace_size(2, 3, 100, 64, fa.DTYPE_BF16) == 2 * 3 * 100 * 65 * 4 * 16
+    lib = fa._load()
+    rc = lib.fa_fwd_ws(Q, K, V, O, LSE, 2, 3, 3, 100, 64, 0.125, 0, None, None, None, fa.DTYPE_BF16,
+                       ws, nbytes)
+    assert rc == status

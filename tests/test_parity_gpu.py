@@ -53,7 +53,7 @@ def to_dev(x, dtype):
     return t.to(tdt).cuda()
 
 
-def run(inp, dtype="bf16", Br=0, Bc=0, scale=None, causal=None):
+def run(inp, dtype="bf16", Br=0, Bc=0, scale=None, causal=None, workspace=None):
     q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
     kl = torch.from_numpy(inp["key_len"]).cuda() if inp.get("key_len") is not None else None
     bm = torch.from_numpy(inp["block_mask"]).cuda() if inp.get("block_mask") is not None else None
@@ -62,9 +62,15 @@ def run(inp, dtype="bf16", Br=0, Bc=0, scale=None, causal=None):
     sc = float(inp["scale"] if scale is None else scale)
     cz = inp["causal"] if causal is None else causal
     fa.fwd(q, k, v, causal=cz, key_len=kl, block_mask=bm, scale=sc, Br=Br, Bc=Bc,
-           out=out, lse=lse)
+           out=out, lse=lse, workspace=workspace)
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def garbage_workspace(nbytes):
+    """A workspace whose bytes are all 0xFF (NaN as fp32): any partial result
+    the split forgets to write shows up as a non-finite output."""
+    return torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
 
 
 def ref(inp, scale=None, causal=None):
@@ -449,3 +455,59 @@ def test_nonascending_tile_order_fully_masked_rows(order):
     out, lse = fa.fwd(q, k, v, key_len=kl, Br=32, Bc=64, tile_order=ORDERS[order])
     torch.cuda.synchronize()
     check(out.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), TOL_BF16, f"{order} masked")
+
+
+
+# ---------------------------------------------------------------- key-range split (fa_fwd_ws)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 129, 300, 1000])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_split_forward_modes(d, N, mode):
+    """Small grids take the split: 2..8 query tiles -> 16 shares, so many
+    shares are empty or fully masked (LSE_s = -inf, weight 0)."""
+    inp = custom(2, 3, N, d, seed=100 + N + d, **modes_for(N, 101)[mode])
+    need = fa.fa_fwd_workspace_size(2, 3, N, d, fa.DTYPE_BF16)
+    assert need > 0
+    o, lse = run(inp, workspace=garbage_workspace(need))
+    check(o, lse, *ref(inp), TOL_BF16, f"split d={d} N={N} {mode}")
+
+
+def test_split_forward_fully_masked_rows():
+    inp = custom(2, 2, 200, 128, seed=102, key_len=[0, 130])
+    o, lse = run(inp, workspace=True)
+    check(o, lse, *ref(inp), TOL_BF16, "split masked")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_forward_f16_and_gqa(d):
+    inp = custom(1, 4, 777, d, seed=103, dtype="f16", causal=True)
+    o, lse = run(inp, dtype="f16", workspace=True)
+    check(o, lse, *ref(inp), TOL_F16, f"split f16 d={d}")
+    q, k, v, _ = random_qkv(2, 8, 500, d, 104, "bf16")
+    k, v = k[:, :2].copy(), v[:, :2].copy()
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = fa.fwd(tq, tk, tv, causal=True, scale=scale, workspace=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_f64(q, k, v, scale, True)
+    check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, TOL_BF16, "split gqa")
+
+
+@pytest.mark.parametrize("H,N,d,causal", [(2, 16384, 128, True), (1, 32768, 128, True), (2, 16384, 64, False)])
+def test_split_forward_one_gpu_share_sampled_rows(H, N, d, causal):
+    """The one-GPU share of a head-sharded 16K problem, and a single 32K
+    head, at full size: sampled rows against the oracle, all rows finite,
+    and the whole output within the bar of the unsplit kernel's."""
+    inp = custom(1, H, N, d, seed=105 + H, causal=causal, amp=0.5)
+    need = fa.fa_fwd_workspace_size(1, H, N, d, fa.DTYPE_BF16)
+    assert need > 0
+    rows = sample_rows(1, H, N, seed=106, per_head=24)
+    o_ref, lse_ref = oracle.attention_rows_f64(inp["q"], inp["k"], inp["v"], rows,
+                                               float(inp["scale"]), causal, None, None, 128)
+    o, lse = run(inp, workspace=garbage_workspace(need))
+    check(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, TOL_BF16, f"split H={H} N={N}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    o1, lse1 = run(inp)
+    assert np.abs(o - o1).max() <= TOL_BF16 and np.abs(lse - lse1).max() <= TOL_LSE
