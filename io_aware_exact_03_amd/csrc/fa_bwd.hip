@@ -31,10 +31,13 @@
 //    key tiles (64 keys of K and V staged in LDS per step, taken as two
 //    32-key chunks).  Per chunk: S^T = K Q^T, dP^T = V dO^T (lane = query),
 //    then dQ^T += K^T dS^T.
+//  * bwd_reduce: with a query-head split of grouped heads (fa_bwd_ex with a
+//    workspace), the dK/dV kernels write fp32 partials per split and this
+//    kernel adds them in split order and rounds once.
 // Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics
 // and no fp32 scratch for dQ, and keeps the results deterministic.
 //
-// Layouts of the 32x32x16 bf16 matrix-core product (fp32 accumulate) are
+// Layouts of the 32x32x16 bf16 / fp16 matrix-core products (fp32 accumulate) are
 // those of the forward kernels: a product's 16 accumulator values per lane
 // are one column (lane % 32) and 16 rows; fed back as the B operand of the
 // next product, 8 of them give the 16-row reduction block with the row

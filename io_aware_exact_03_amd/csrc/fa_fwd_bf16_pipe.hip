@@ -24,6 +24,10 @@
 //  * Scores are computed transposed (S^T = K Q^T) so each lane holds one
 //    query row: the row max is an in-lane v_max3 chain plus one
 //    v_permlane32_swap; O^T += V^T P^T takes P straight from registers.
+//  * SPLIT = true (fa_fwd_ws, grids too small for the GPU): the workgroup
+//    covers one share of its query tile's key tiles and writes an fp32
+//    partial O and partial LSE; fwd_merge combines the shares of each row
+//    by log-sum-exp.
 #include "fa_bf16_tiles.h"
 
 namespace fa {
