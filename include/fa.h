@@ -234,12 +234,14 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
  *               other step as for bf16).  Other dtypes:
  *               FA_ERR_UNSUPPORTED_TILE.
  *   workspace : DEVICE memory owned by the caller (16-byte aligned) of
- *               workspace_bytes bytes, or NULL.  With grouped heads and a
- *               small key/value grid (few key/value heads, short N), the
- *               query heads of each group are then split over several
- *               workgroups that write fp32 partial dK, dV here; a second
- *               kernel adds them in a fixed order (deterministic) and rounds
- *               once.  fa_bwd_workspace_size gives the bytes needed; when it
+ *               workspace_bytes bytes, or NULL.  When a grid is too small
+ *               for the GPU (few heads or key/value heads, short N), the
+ *               work of each dK/dV workgroup (its query heads and query
+ *               tiles) and of each dQ workgroup (its key tiles) is then
+ *               split over several workgroups that write fp32 partials
+ *               here; reduce kernels add them in a fixed order
+ *               (deterministic) and round once.  fa_bwd_workspace_size
+ *               gives the bytes needed; when it
  *               is 0, or workspace is NULL, no workspace is used and the
  *               result is that of fa_bwd.  A non-NULL workspace smaller than
  *               needed, misaligned, or overlapping an input or output:

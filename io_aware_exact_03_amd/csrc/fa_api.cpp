@@ -191,7 +191,13 @@ int backward(const void *q, const void *k, const void *v, const void *o, const v
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     a.nsplit = split ? fa::bwd_split(B, H, Hkv, N) : 1;
-    a.part = split ? static_cast<float *>(workspace) : nullptr;
+    a.nsplit_q = split ? fa::bwd_split_q(B, H, N) : 1;
+    a.part = split && a.nsplit > 1 ? static_cast<float *>(workspace) : nullptr;
+    a.part_q = nullptr;
+    if (split && a.nsplit_q > 1) {
+        const uint64_t kv_part = a.nsplit > 1 ? (uint64_t)a.nsplit * 2 * B * Hkv * (uint64_t)N * d : 0;
+        a.part_q = static_cast<float *>(workspace) + kv_part;
+    }
     const hipError_t err = fa::launch_bwd(a, d, causal ? 1 : 0, dtype == FA_DTYPE_F16 ? 1 : 0, stream);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;

@@ -254,13 +254,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     const int qt_first = CAUSAL ? k0 / BQ : 0;
     const int nqt = (N + BQ - 1) / BQ;
     const int steps_per_head = nqt - qt_first;
-    // This workgroup's query heads: group / nsplit of the group.
-    const int gsplit = a.group / a.nsplit;
-    // workgroup-uniform (every wave takes part in the copies and barriers)
-    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * gsplit;
+    // Steps (query head g of the group, query tile) in head-major order;
+    // this workgroup takes the contiguous range [s_lo, nsteps) of its split.
+    // Workgroup-uniform (every wave takes part in the copies and barriers).
+    const int total = k0 >= kv_len ? 0 : steps_per_head * a.group;
+    const int s_lo = (int)((int64_t)total * split / a.nsplit);
+    const int nsteps = (int)((int64_t)total * (split + 1) / a.nsplit);
     auto step_tile = [&](int s, int *hq, int *qt) {
         const int g = s / steps_per_head;
-        *hq = b * a.H + hkv * a.group + split * gsplit + g;
+        *hq = b * a.H + hkv * a.group + g;
         *qt = qt_first + (s - g * steps_per_head);
     };
     auto tile_active = [&](int qt) {
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
         return s;
     };
 
-    int s = next_step(0);
+    int s = next_step(s_lo);
     if (s < nsteps) issue(s, 0);
     int buf = 0;
     while (s < nsteps) {
@@ -465,11 +467,13 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     const int qt_first = CAUSAL ? k0 / BQ : 0;
     const int nqt = (N + BQ - 1) / BQ;
     const int steps_per_head = nqt - qt_first;
-    const int gsplit = a.group / a.nsplit;
-    const int nsteps = k0 >= kv_len ? 0 : steps_per_head * gsplit;
+    // Steps in head-major order; this workgroup's split takes [s_lo, nsteps).
+    const int total = k0 >= kv_len ? 0 : steps_per_head * a.group;
+    const int s_lo = (int)((int64_t)total * split / a.nsplit);
+    const int nsteps = (int)((int64_t)total * (split + 1) / a.nsplit);
     auto step_tile = [&](int s, int *hq, int *qt) {
         const int g = s / steps_per_head;
-        *hq = b * a.H + hkv * a.group + split * gsplit + g;
+        *hq = b * a.H + hkv * a.group + g;
         *qt = qt_first + (s - g * steps_per_head);
     };
     auto tile_active = [&](int qt) {
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
         return s;
     };
 
-    int s = next_step(0);
+    int s = next_step(s_lo);
     if (s < nsteps) issue(s, 0);
     wait_copies();
     __syncthreads();
@@ -635,6 +639,20 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     }
 }
 
+// Sum of the nsplit_q fp32 partials of dQ, times the scale, rounded once.
+template <class T>
+__global__ __launch_bounds__(256) void bwd_reduce_dq(BwdArgs a, int64_t el) {
+    using x4_t = typename Elem<T>::x4;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= el) return;
+    f32x4_t sq = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.nsplit_q; ++s) sq += *reinterpret_cast<const f32x4_t *>(a.part_q + (int64_t)s * el + i);
+    x4_t w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (T)(sq[j] * a.scale);
+    *reinterpret_cast<x4_t *>(reinterpret_cast<T *>(a.dq) + i) = w;
+}
+
 // ---------------------------------------------------------------- dQ
 
 template <class T, int D, int NW, int KT, bool CAUSAL>
@@ -651,8 +669,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = a.N;
     const int nqt = (N + BR - 1) / BR;
-    int bh, qt;
-    tile_of_block(nqt, CAUSAL, &bh, &qt);
+    // (query tile, key-range split): the splits of one query tile adjacent,
+    // heads and tiles in the XCD-aware order, causal tiles longest first.
+    const int item = xcd_item(nqt * a.nsplit_q);
+    const int split = item % a.nsplit_q;
+    const int rest = item / a.nsplit_q;
+    const int bh = rest / nqt;
+    const int qt = CAUSAL ? nqt - 1 - (rest - bh * nqt) : rest - bh * nqt;
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
@@ -668,7 +691,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     if (a.key_len) kv_len = min(max(a.key_len[b], 0), N);
     int kv_end = kv_len;
     if (CAUSAL) kv_end = min(kv_end, q0 + BR);
-    const int ntiles = (kv_end + BKT - 1) / BKT;
+    const int nall = (kv_end + BKT - 1) / BKT;
+    // Key steps [t_lo, ntiles) of this split (all of them when unsplit).
+    const int t_lo = (int)((int64_t)nall * split / a.nsplit_q);
+    const int ntiles = (int)((int64_t)nall * (split + 1) / a.nsplit_q);
 
     // This wave's 32 query rows as B operands: Q^T and dO^T fragments.
     x8_t qf[NQK], dof[NQK];
@@ -711,7 +737,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
         copy_rows<D, NW, BKT>(V, t * BKT, kv_len, v_lds[buf], wave, lane);
     };
 
-    int t = next_tile(0);
+    int t = next_tile(t_lo);
     if (t < ntiles) issue(t, 0);
     int buf = 0;
     while (t < ntiles) {
@@ -765,7 +791,19 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
         buf ^= 1;
     }
 
-    if (qrow < N) {
+    if (qrow < N && a.nsplit_q > 1) {
+        // fp32 partial of this key-range split (before the scale)
+        float *pq = a.part_q + ((int64_t)split * a.B * a.H * N) * D + head + (int64_t)qrow * D;
+#pragma unroll
+        for (int mb = 0; mb < ND; ++mb)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                f32x4_t w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] = dq[mb][4 * gg + j];
+                *reinterpret_cast<f32x4_t *>(pq + mb * 32 + 8 * gg + 4 * (lane / 32)) = w;
+            }
+    } else if (qrow < N) {
         const float scale = a.scale;
         T *dQ = reinterpret_cast<T *>(a.dq) + head + (int64_t)qrow * D;
 #pragma unroll
@@ -807,8 +845,12 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     }
     const int nqt = (a.N + 32 * NW - 1) / (32 * NW);
     constexpr int KT = 2;
-    hipLaunchKernelGGL((bwd_dq<T, D, NW, KT, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H)), dim3(NW * 64), 0, stream,
-                       a);
+    hipLaunchKernelGGL((bwd_dq<T, D, NW, KT, CAUSAL>), dim3((unsigned)(nqt * a.B * a.H * a.nsplit_q)),
+                       dim3(NW * 64), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit_q == 1) return e;
+    const int64_t el = (int64_t)a.B * a.H * a.N * D;
+    hipLaunchKernelGGL((bwd_reduce_dq<T>), dim3((unsigned)((el / 4 + 255) / 256)), dim3(256), 0, stream, a, el);
     return hipGetLastError();
 }
 
@@ -821,27 +863,38 @@ hipError_t launch_bwd_typed(const BwdArgs &a, int d, int causal, hipStream_t str
 
 }  // namespace
 
-// A query-head split pays when the dK/dV grid (one workgroup per key/value
-// head and 128-key block, one workgroup per CU) is small: if the unsplit
-// grid has fewer than 512 workgroups, the largest divisor of the group that
-// keeps the grid within 2048.  (Measured: splitting a grid that already has
-// 512 made the backward slower; multi-query at 16K gained 1.6x at 1024
-// workgroups and 5 % more at 2048.)
+// Splits pay when a grid is too small for the GPU (one dK/dV workgroup per
+// CU; few heads, few key/value heads, or short sequences).  For each of the
+// dK/dV grid (B * H_kv * 128-key blocks) and the dQ grid (B * H * 128-row
+// tiles): if it has fewer than 512 workgroups, the largest power of two up
+// to 16 that keeps it within 1024.  Measured on B1 H2 N16384 causal: dK/dV
+// split 4 and dQ split 4, 709 us; 8 and 4, 779 us; 16 and 4, 910 us; 8 and
+// 8, 805 us; unsplit 1145 us.  Multi-query at 16K: 8 splits 3957 us, 16
+// splits 4063 us, unsplit 10951 us.  Splitting a 512-workgroup grid made it
+// slower.
+static int pow2_split(int64_t base, int64_t cap) {
+    if (base >= 512) return 1;
+    int s = 1;
+    while (s < 16 && base * s * 2 <= cap) s *= 2;
+    return s;
+}
+
 int bwd_split(int B, int H, int Hkv, int N) {
     if (B < 1 || H < 1 || Hkv < 1 || N < 1 || H % Hkv != 0) return 1;
-    const int64_t base = (int64_t)B * Hkv * ((N + 127) / 128);
-    const int group = H / Hkv;
-    if (group == 1 || base >= 512) return 1;
-    int best = 1;
-    for (int s = 2; s <= group; ++s)
-        if (group % s == 0 && base * s <= 2048) best = s;
-    return best;
+    return pow2_split((int64_t)B * Hkv * ((N + 127) / 128), 1024);
+}
+
+int bwd_split_q(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1) return 1;
+    return pow2_split((int64_t)B * H * ((N + 127) / 128), 1024);
 }
 
 uint64_t bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
-    const int s = bwd_split(B, H, Hkv, N);
-    if (s == 1) return 0;
-    return (uint64_t)s * 2 * (uint64_t)B * Hkv * (uint64_t)N * d * sizeof(float);
+    const int s = bwd_split(B, H, Hkv, N), sq = bwd_split_q(B, H, N);
+    uint64_t bytes = 0;
+    if (s > 1) bytes += (uint64_t)s * 2 * (uint64_t)B * Hkv * (uint64_t)N * d * sizeof(float);
+    if (sq > 1) bytes += (uint64_t)sq * (uint64_t)B * H * (uint64_t)N * d * sizeof(float);
+    return bytes;
 }
 
 hipError_t launch_bwd(const BwdArgs &a, int d, int causal, int f16, hipStream_t stream) {

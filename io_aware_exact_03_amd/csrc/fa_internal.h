@@ -54,17 +54,24 @@ struct BwdArgs {
     int nkb;
     float scale;       // softmax scale
     float scale_log2;  // scale * log2(e)
-    // Query-head split of each key/value head's group: nsplit workgroups per
-    // key block each take group / nsplit query heads and write fp32 partial
-    // dK (before the scale) and dV to part ([nsplit][2][B*Hkv*N*d], dK then
-    // dV); a reduce kernel adds them.  nsplit = 1: no split, part unused.
+    // Splits for grids too small for the GPU (fa_bwd_ex with a workspace).
+    // dK/dV: the sequence of (query head, query tile) steps of each key
+    // block is cut into nsplit contiguous ranges, one workgroup each, writing
+    // fp32 partial dK (before the scale) and dV to part
+    // ([nsplit][2][B*Hkv*N*d], dK then dV).  dQ: the key tiles of each
+    // query tile are cut into nsplit_q ranges, writing fp32 partial dQ
+    // (before the scale) to part_q ([nsplit_q][B*H*N*d]).  Reduce kernels
+    // add the partials.  1: no split, the buffer is unused.
     int nsplit;
     float *part;
+    int nsplit_q;
+    float *part_q;
 };
 
-// Query-head split the backward uses for a shape when given a workspace, and
-// the workspace bytes it then needs (0 when no split is worth it).
+// Splits the backward uses for a shape when given a workspace (dK/dV and
+// dQ), and the workspace bytes they then need (0 when no split is worth it).
 int bwd_split(int B, int H, int Hkv, int N);
+int bwd_split_q(int B, int H, int N);
 uint64_t bwd_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 // Enqueues the backward kernels on `stream`.

@@ -45,7 +45,7 @@ def main():
         tq, tk, tv = dev(inp["q"], tdt), dev(inp["k"], tdt), dev(inp["v"], tdt)
         tdo = dev(dout, tdt)
         o, lse = fa.fwd(tq, tk, tv, causal=True)
-        dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True)
+        dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True, workspace=None)
         torch.cuda.synchronize()
         ref = oracle.attention_bwd_f64(inp["q"], inp["k"], inp["v"], tdo.float().cpu().numpy(),
                                        float(inp["scale"]), True)

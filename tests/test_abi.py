@@ -154,15 +154,18 @@ def test_bwd_ex_rejects_unbuilt_dtypes(dtype):
 WS = 0x78000000
 
 
+BWS = 2 * 16 * 2 * 2 * 100 * 64 * 4 + 16 * 2 * 4 * 100 * 64 * 4
+
+
 @pytest.mark.parametrize("ws,nbytes,status", [
-    (WS, 409600 - 1, 7),        # smaller than fa_bwd_workspace_size
-    (WS + 8, 409600, 7),        # not 16-byte aligned
-    (DQ + 64, 409600, 7),       # over an output
-    (Q, 409600, 7),             # over an input
+    (WS, BWS - 1, 7),           # smaller than fa_bwd_workspace_size
+    (WS + 8, BWS, 7),           # not 16-byte aligned
+    (DQ + 64, BWS, 7),          # over an output
+    (Q, BWS, 7),                # over an input
 ])
 def test_bwd_workspace_validation(ws, nbytes, status):
-    # B2 H4 H_kv2 N100 d64: grouped heads on a tiny grid, so a split is used
-    assert fa.fa_bwd_workspace_size(2, 4, 2, 100, 64) == 409600
+    # B2 H4 H_kv2 N100 d64: a tiny grid, so both splits are used (16 each)
+    assert fa.fa_bwd_workspace_size(2, 4, 2, 100, 64) == BWS
     lib = fa._load()
     rc = lib.fa_bwd_ex(Q, K, V, O, DO, LSEB, DELTA, DQ, DK, DV, 2, 4, 2, 100, 64, 0.125, 0, None, None,
                        None, fa.DTYPE_BF16, ws, nbytes)
@@ -171,17 +174,18 @@ def test_bwd_workspace_validation(ws, nbytes, status):
 
 def test_bwd_workspace_size():
     size = fa.fa_bwd_workspace_size
-    # plain multi-head attention never splits
+    # grids with at least 512 workgroups are not split
     assert size(1, 16, 16, 16384, 128) == 0 and size(8, 12, 12, 1024, 64) == 0
-    # multi-query 16K: 128 key blocks; the largest divisor of 16 keeping the
-    # grid within 2048 workgroups is 16 -> 16 splits x (dK, dV) x N x d floats
-    assert size(1, 16, 1, 16384, 128) == 16 * 2 * 16384 * 128 * 4
-    # four key/value heads at 16K already give 512 workgroups: no split
+    # four key/value heads at 16K already give 512 dK/dV workgroups
     assert size(1, 16, 4, 16384, 128) == 0
-    # 8 query heads per key/value head, 2 x 32 key blocks = 64 -> 8 splits
+    # multi-query 16K: 128 dK/dV workgroups -> 8 splits x (dK, dV) x N x d
+    # floats; the dQ grid (16 x 128 tiles) needs none
+    assert size(1, 16, 1, 16384, 128) == 8 * 2 * 16384 * 128 * 4
+    # 2 x 2 x 32 = 128 key blocks -> 8 dK/dV splits; dQ grid 1024: none
     assert size(2, 16, 2, 4096, 64) == 8 * 2 * 2 * 2 * 4096 * 64 * 4
-    # 12 query heads per key/value head on 1 x 100 key blocks -> 12 splits
-    assert size(1, 12, 1, 12800, 64) == 12 * 2 * 12800 * 64 * 4
+    # one GPU's share of a head-sharded 16K problem: 256 dK/dV workgroups
+    # -> 4 splits; 256 dQ workgroups -> 4 key-range splits of dQ
+    assert size(1, 2, 2, 16384, 128) == 4 * 2 * 2 * 16384 * 128 * 4 + 4 * 2 * 16384 * 128 * 4
     # invalid shapes report 0
     assert size(0, 4, 2, 100, 64) == 0 and size(1, 4, 3, 100, 64) == 0 and size(1, 4, 2, 100, 96) == 0
 

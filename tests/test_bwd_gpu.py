@@ -40,7 +40,7 @@ def dev(x, dtype="bf16"):
 
 
 def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None, scale=None,
-             dtype="bf16", workspace=True):
+             dtype="bf16", workspace=None):
     q, _, _, rng = random_qkv(B, H, N, d, seed, dtype)
     _, k, v, rng = random_qkv(B, H_kv, N, d, seed + 1, dtype, rng=rng)
     dout = rng.standard_normal(q.shape).astype(np.float32)
@@ -88,6 +88,19 @@ def modes(N, seed):
 @pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
 def test_bwd_modes(d, N, mode):
     run_case(2, 2, 2, N, d, seed=70 + N + d, **modes(N, 71)[mode])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 45, 300, 1000])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_bwd_modes_split(d, N, mode):
+    """Small grids with a workspace: the dK/dV steps and the dQ key range
+    are both split (16 ways here), partials summed by the reduce kernels;
+    the workspace starts full of NaN bytes."""
+    need = fa.fa_bwd_workspace_size(2, 2, 2, N, d)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    run_case(2, 2, 2, N, d, seed=110 + N + d, workspace=ws, **modes(N, 111)[mode])
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -270,3 +283,33 @@ def test_mqa_block_sparse_full_size_sampled():
         err = float(np.abs(g - r).max())
         bound = TOL_REL * max(1.0, float(np.abs(r).max()))
         assert err <= bound, f"MQA {name}: max|dg| = {err:.3e} > {bound:.3e}"
+
+
+
+@pytest.mark.parametrize("H,N", [(2, 16384), (1, 32768)])
+def test_bwd_one_gpu_share_split_sampled(H, N):
+    # One GPU's share of a head-sharded problem (B1 H2 N16384) and a single
+    # 32K head, causal, d = 128: the backward splits both the dK/dV steps and
+    # the dQ key range.  dQ on sampled rows, dK and dV on sampled keys.
+    B, d = 1, 128
+    assert fa.fa_bwd_workspace_size(B, H, H, N, d) > 0
+    rng = np.random.Generator(np.random.PCG64(3200 + H))
+    q, k, v, rng = random_qkv(B, H, N, d, 0, "bf16", 0.5, rng=rng)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    tdo = dev(rng.standard_normal(q.shape, dtype=np.float32))
+    o, lse = fa.fwd(tq, tk, tv, causal=True, scale=scale)
+    dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = rng.choice(B * H * N, size=24, replace=False)
+    cols = int(rng.integers(B * H)) * N + np.unique(np.concatenate([[0, N - 1], rng.choice(N, 6)]))
+    dout = tdo.float().cpu().numpy()
+    ref = {"dq": oracle.attention_bwd_rows_f64(q, k, v, dout, rows, scale, True)}
+    ref["dk"], ref["dv"] = oracle.attention_bwd_cols_f64(q, k, v, dout, cols, scale, True)
+    rows_t, cols_t = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    got = {"dq": dq.reshape(-1, d)[rows_t], "dk": dk.reshape(-1, d)[cols_t], "dv": dv.reshape(-1, d)[cols_t]}
+    for name, r in ref.items():
+        g = got[name].double().cpu().numpy()
+        err = float(np.abs(g - r).max())
+        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        assert err <= bound, f"H={H} N={N} {name}: max|dg| = {err:.3e} > {bound:.3e}"
