@@ -13,16 +13,9 @@
 //    bf16 and sums the rows.  Each step is a fixed sequence of matrix-core
 //    slots with the VALU work spread over them (see `step`), so one wave
 //    keeps both pipes busy by itself.
-//  * The softmax reference point m of a row (the value subtracted before
-//    exponentiating) moves only when a tile's maximum exceeds it by more
-//    than kRefSlack (base-2 units).  Otherwise the tile's probabilities are
-//    taken against the old m, so they may reach 2^kRefSlack instead of 1:
-//    O and l carry the same factor, which cancels in O / l and in
-//    m + log2(l), so the result is the same up to rounding.  The rescale
-//    factor is then exactly 1 for every row of the wave and the multiply
-//    of O is skipped.  With m the exact running maximum (a slack of 0) 42 %
-//    (d = 64) to 75 % (16K causal, d = 128) of the wave-tiles rescaled;
-//    with the slack almost none do after the first tile.
+//  * O is rescaled only when some row of the wave raised its running
+//    maximum; otherwise the rescale factor is exactly 1 and the multiply is
+//    skipped (a bit-identical no-op).
 //  * Each wave owns 32 query rows; a workgroup of NW waves owns 32*NW.
 //  * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging) through an NSTAGE-deep ring: K runs one tile ahead of V (it is
@@ -271,10 +264,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     // and the first allowed key makes alpha = exp2(-huge) = 0 while O and l
     // are still 0.  Rows that never see a key keep l = 0 (LSE = -inf, O = 0).
     float m = -__FLT_MAX__, l = 0.f;
-    // Probabilities may reach 2^kRefSlack (see the header): l and O lose 8 of
-    // fp32's 128 binary orders of headroom, and P in bf16 keeps its relative
-    // precision at any scale.
-    constexpr float kRefSlack = 8.f;
     // Scores ping-pong between sA and sB across consecutive iterations.
     acc_t sA[NKB], sB[NKB];
 
@@ -352,16 +341,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
             } else if constexpr (kind == kChunkRed) {
                 // Row max over the partner lane (permlane32 swap), scaled
                 // by c > 0 before the max: one three-way max, no -inf guards.
-                // Both lanes of a row get the same value.
                 const auto r = __builtin_amdgcn_permlane32_swap(f2u(mx), f2u(mx), false, false);
-                const float m_max = fmaxf(fmaxf(m, u2f(r[0]) * c), u2f(r[1]) * c);
-                // New reference only beyond the slack (the first allowed key
-                // always moves it: -FLT_MAX + slack rounds to -FLT_MAX).
-                const float m_new = m_max > m + kRefSlack ? m_max : m;
+                const float m_new = fmaxf(fmaxf(m, u2f(r[0]) * c), u2f(r[1]) * c);
                 alpha = fast_exp2(m - m_new);
                 neg_m = -m_new;
                 m = m_new;
-                // O needs rescaling only when some row's reference moved
+                // O needs rescaling only when some row's maximum moved
                 // (alpha = 1 exactly otherwise).
                 rescale = wave_any(alpha != 1.f);
                 pin(alpha);
