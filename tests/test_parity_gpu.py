@@ -17,7 +17,8 @@ torch = pytest.importorskip("torch")
 
 import io_aware_exact_03_amd as fa  # noqa: E402
 import oracle  # noqa: E402
-from workloads import WORKLOADS, make_inputs, random_qkv, band_global_block_mask, causal_prefix  # noqa: E402
+from workloads import (WORKLOADS, make_inputs, random_qkv, band_global_block_mask, causal_prefix,  # noqa: E402
+                       bf16_round, f16_round)
 
 pytestmark = pytest.mark.gpu
 
@@ -254,6 +255,52 @@ def test_dominant_logit_selects_value_row():
     np.testing.assert_allclose(o, np.broadcast_to(inp["v"][:, :, jstar:jstar + 1], o.shape),
                                rtol=0, atol=TOL_BF16)
     np.testing.assert_allclose(lse, 40.0, rtol=0, atol=TOL_LSE)
+
+
+def _score_profile(name, N):
+    """Designed per-key logits (natural-log units, before any max shift)."""
+    j = np.arange(N, dtype=np.float64)
+    t = j // 64  # key tile of 64
+    return {
+        # the row max creeps up by ~0.9 (base 2) per key tile: a small
+        # rescale of O on almost every tile
+        "slow_rise": 0.01 * j,
+        # every key tile's max is ~17 (base 2) above the last one's: O and l
+        # shrink by ~2^-17 on every tile
+        "jumps": 12.0 * t,
+        # the first tile holds the max: no rescale after it
+        "falling": -0.02 * j,
+        # rises, steps and drops mixed
+        "sawtooth": 6.0 * (t % 3) + 0.01 * j,
+    }[name]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("profile", ["slow_rise", "jumps", "falling", "sawtooth"])
+def test_running_maximum_profiles(profile, causal, dtype):
+    """Logits whose per-tile maxima rise slowly, jump far from tile to tile,
+    fall or alternate, up to ~180 (natural log): the running maximum, the
+    rescale (taken or skipped per wave) and the running sum must give the
+    oracle's O and LSE whatever path the maxima take, in the direct launch
+    and in the key-range split."""
+    B, H, N, d = 1, 2, 1024, 64
+    rnd = {"bf16": bf16_round, "f16": f16_round}[dtype]
+    rng = np.random.default_rng(40 + len(profile))
+    q = 0.3 * rng.standard_normal((B, H, N, d))
+    k = 0.3 * rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    scale = 0.125
+    q[..., 0] = 8.0  # q . k ~ 8 * k[..., 0], times the scale: logit ~ k[..., 0]
+    k[..., 0] = _score_profile(profile, N)
+    inp = dict(q=rnd(q.astype(np.float32)), k=rnd(k.astype(np.float32)), v=rnd(v.astype(np.float32)),
+               causal=causal, key_len=None, block_mask=None, scale=np.float32(scale))
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F16
+    want = ref(inp)
+    check(*run(inp, dtype), *want, tol, f"{profile} {dtype}")
+    need = fa.fa_fwd_workspace_size(B, H, N, d, fa.DTYPE_BF16 if dtype == "bf16" else fa.DTYPE_F16)
+    assert need > 0
+    check(*run(inp, dtype, workspace=garbage_workspace(need)), *want, tol, f"{profile} {dtype} split")
 
 
 def test_ones_value_column_gives_ones():
