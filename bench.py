@@ -15,7 +15,10 @@ Prints ONE JSON line:
               separate pass after the timed region);
               traffic = measured HBM bytes per launch from the committed
               rocprofv3 counter summary if it was taken on the current
-              kernel sources, else null
+              kernel sources, else null; likewise sclk_ghz, the shader clock
+              the kernel ran at in that counter run (GPU-busy cycles per
+              XCD over the dispatch time), with the matrix-core peak at that
+              clock (256 CUs x sclk x 4096 FLOP/clk) and the fraction of it
   cpu_baseline the FP64 oracle timed on the host cores on a bounded sample
               of query rows of the same workload, in the same unit; the
               GPU/oracle deviation on those rows is reported beside it
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 # Dense bf16 matrix-core peak of MI355X: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
+BF16_FLOP_PER_CLK = 256 * 4096
 PEAK_F32_MFMA_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["fa_common.h", "fa_internal.h", "fa_bf16_tiles.h", "fa_fwd_bf16.hip",
@@ -47,9 +51,9 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed counter summary, or None when
-    it is missing or was taken on different kernel sources."""
+def _profiled(workload, key):
+    """A figure of the committed counter summary for this workload, or None
+    when it is missing or was taken on different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -58,7 +62,28 @@ def measured_traffic(workload):
     entry = t.get(workload)
     if not entry or entry.get("source_sha256") != kernel_source_hash():
         return None
-    return entry.get("bytes_per_launch")
+    return entry.get(key)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)."""
+    return _profiled(workload, "bytes_per_launch")
+
+
+def measured_sclk(workload):
+    """Shader clock (GHz) of the counter run: GRBM_GUI_ACTIVE / 8 XCDs over
+    the dispatch time."""
+    return _profiled(workload, "sclk_ghz")
+
+
+def sclk_fields(achieved, workload, dtype):
+    """The matrix-core peak at the profiled shader clock, and the fraction
+    of it reached (bf16 only; None when no valid counter run exists)."""
+    ghz = measured_sclk(workload) if dtype == "bf16" else None
+    if not ghz:
+        return {"sclk_ghz": None, "peak_at_sclk": None, "frac_at_sclk": None}
+    peak = BF16_FLOP_PER_CLK * ghz * 1e9 / 1e12
+    return {"sclk_ghz": round(ghz, 3), "peak_at_sclk": round(peak, 1), "frac_at_sclk": round(achieved / peak, 4)}
 
 
 def algorithmic_bytes(w, inp):
@@ -257,6 +282,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.key),
+                     **sclk_fields(achieved, w.key, w.dtype),
                      "kernel_ms": round(kern_ms, 5),
                      "launch_ms_p10_p50_p90": [round(pct(10), 5), round(pct(50), 5), round(pct(90), 5)],
                      "algorithmic_bytes": algorithmic_bytes(w, inp)},
