@@ -99,6 +99,18 @@ def algorithmic_bytes(w, inp):
     return q_o + 2 * kv_rows * d * elem
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp, o_gpu, lse_gpu, seconds, seed):
     """Oracle on batches of sampled query rows until `seconds` have passed."""
     import numpy as np
@@ -151,7 +163,7 @@ def cpu_baseline(w, inp, o_gpu, lse_gpu, seconds, seed):
             break
         batch = min(4096, batch * 2)
     tflops = flop / elapsed / 1e12 if elapsed > 0 else None
-    return dict(value=tflops, unit="TFLOP/s", cores=oracle.threads(), kind="oracle",
+    return dict(value=tflops, unit="TFLOP/s", cores=oracle.threads(), cpu_model=cpu_model(), kind="oracle",
                 sample=f"{done} query rows of {total_rows} (uniform without replacement, seed "
                        f"{seed}), FP64 C oracle, {elapsed:.1f} s, {flop / 1e9:.2f} GFLOP "
                        f"algorithmic"), max_do, max_dlse, done
