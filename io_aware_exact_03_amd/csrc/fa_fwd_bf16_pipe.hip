@@ -222,21 +222,36 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     auto kstage = [&](int s) { return s == 0 ? k_lds0 : s == 1 ? k_lds1 : s == 2 ? k_lds2 : k_lds3; };
     auto vstage = [&](int s) { return s == 0 ? v_lds0 : s == 1 ? v_lds1 : s == 2 ? v_lds2 : v_lds3; };
 
-    // Q fragments (B operand of S^T = K Q^T), sign-folded so that c >= 0.
+    // Prologue loads, ordered so that their round trips overlap: the first
+    // mask chunk (block-sparse), then this wave's Q rows, and only then the
+    // ballot that needs the mask (it waits for the mask load alone).  The Q
+    // values are not touched before the first K/V copies have been issued
+    // and have landed, so the Q latency hides under the copies' latency.
+    // Rows past N load row N-1 and are zeroed when the fragments are formed.
+    const int qrow = wq0 + lane % 32;
+    const int pre_chunk = ((tbeg * BC) >> 7) >> 6;
+    uint8_t mask_pre = 0;
+    if (mrow) mask_pre = mrow[min(pre_chunk * 64 + lane, a.nkb - 1)];
+    u32x4_t qraw[NQK];
+    {
+        const T *qsrc = Q + (int64_t)min(qrow, N - 1) * D + 8 * (lane / 32);
+#pragma unroll
+        for (int ks = 0; ks < NQK; ++ks) qraw[ks] = *reinterpret_cast<const u32x4_t *>(qsrc + ks * 16);
+    }
+    if (mrow) {
+        // The empty asm takes the mask byte as issued by its load: the
+        // compiler's wait for it lands here, after the Q loads (which the
+        // memory clobber keeps above), not right after the load.
+        uint32_t mv = mask_pre;
+        asm volatile("" : "+v"(mv)::"memory");
+        mask_bits = __builtin_amdgcn_ballot_w64(pre_chunk * 64 + lane < a.nkb && mv != 0);
+        mask_chunk = pre_chunk;
+    }
+    // Q fragments (B operand of S^T = K Q^T), sign-folded so that c >= 0;
+    // formed after the first copies (below).
     const float c = scale_factor(a.scale_log2);
     const uint32_t sign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
     x8_t qf[NQK];
-    {
-        const int qrow = wq0 + lane % 32;
-#pragma unroll
-        for (int ks = 0; ks < NQK; ++ks) {
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (qrow < N)
-                x = *reinterpret_cast<const u32x4_t *>(Q + (int64_t)qrow * D + ks * 16 + 8 * (lane / 32));
-            x ^= sign;
-            qf[ks] = __builtin_bit_cast(x8_t, x);
-        }
-    }
 
     // LDS read offsets (elements): K fragment ks of a 32-key block, and the
     // transposed V fragment of output block mb (two 4-row reads, 8 rows apart).
@@ -298,7 +313,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
             // Keep this a branch: the compiler would otherwise if-convert it
             // into per-element selects on every tile.
             asm volatile("" ::);
-            const int qrow = wq0 + lane % 32;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -428,6 +442,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
         if (tq[j] < tend) copy(V, vstage(j), voff, tq[j]);
     wait_copies();
     __syncthreads();
+    {
+        const uint32_t keep = qrow < N ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int ks = 0; ks < NQK; ++ks) qf[ks] = __builtin_bit_cast(x8_t, (qraw[ks] ^ sign) & keep);
+    }
     if (active(tq[0])) qk_plain(sA, kstage(0));
 
     auto iteration = [&](auto stage_tag, acc_t (&s)[NKB], acc_t (&sn)[NKB]) {
@@ -473,7 +492,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     // sum) and partial LSE instead; a share with no allowed key writes
     // O = 0, LSE = -inf, which the merge gives weight 0.
     if constexpr (SPLIT) {
-        const int qrow = wq0 + lane % 32;
         const float l_tot = group_sum<32>(l);
         if (qrow < N) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -493,7 +511,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
         return;
     }
     {
-        const int qrow = wq0 + lane % 32;
         const float l_tot = group_sum<32>(l);
         if (qrow < N) {
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
