@@ -199,6 +199,47 @@ def test_very_long_sequences_sampled_rows(N, d, causal):
               f"N={N} tile study")
 
 
+def _multi_chunk_mask(nb):
+    """Block-mask rows of five kinds, cycling with the query block: active
+    blocks only in the last 64-block chunk, only in the middle chunk, none,
+    a few straddling the chunk boundaries, and every 7th block."""
+    m = np.zeros((nb, nb), dtype=np.uint8)
+    for r in range(nb):
+        kind = r % 5
+        if kind == 0:
+            m[r, nb - 2:] = 1
+        elif kind == 1:
+            m[r, 64 + r % (nb - 64)] = 1
+        elif kind == 3:
+            m[r, [r, 63, 64, 127, nb - 1]] = 1
+        elif kind == 4:
+            m[r, ::7] = 1
+    return m.reshape(-1)
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, False), (128, True)])
+def test_block_mask_rows_over_several_chunks(d, causal):
+    """A 16640-token head has 130 mask blocks per row, which the kernels scan
+    in chunks of 64: rows whose first active block lies in the second or
+    third chunk, empty rows and rows straddling chunk boundaries, direct and
+    with the key-range split (whose shares start inside later chunks);
+    checked on sampled rows of every row kind."""
+    N = 16640
+    nb = N // 128
+    inp = custom(1, 1, N, d, seed=95 + d, causal=causal, amp=0.5, block_mask=_multi_chunk_mask(nb))
+    blocks = [0, 1, 2, 3, 4, 5, 63, 64, 65, 66, 67, 127, 128, 129]
+    rows = np.array(sorted({min(N - 1, r * 128 + o) for r in blocks for o in (0, 77, 127)}), dtype=np.int64)
+    o_ref, lse_ref = oracle.attention_rows_f64(inp["q"], inp["k"], inp["v"], rows, float(inp["scale"]), causal,
+                                               None, inp["block_mask"], 128)
+    assert np.isinf(lse_ref).any() and np.isfinite(lse_ref).any()
+    need = fa.fa_fwd_workspace_size(1, 1, N, d, fa.DTYPE_BF16)
+    assert need > 0
+    for ws in (None, garbage_workspace(need)):
+        o, lse = run(inp, workspace=ws)
+        check(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, TOL_BF16,
+              f"d={d} causal={causal} split={ws is not None}")
+
+
 @pytest.mark.parametrize("H,N,Br", [(2, 4096, 0), (1, 4096, 0), (4, 4096, 64), (2, 4096, 32)])
 def test_heads_spanning_several_xcds(H, N, Br):
     """Few heads: one head's query tiles are shared round-robin by several
