@@ -74,11 +74,6 @@ __device__ __forceinline__ int kv_head_of(int bh, const Args &a) {
     return b * a.Hkv + (bh - b * a.H) / a.group;
 }
 
-// Workgroup -> (head, query tile) order.  Workgroups are handed to the eight
-// XCDs round-robin; when the grid divides evenly, renumber so that each XCD
-// receives one contiguous run of logical tiles (whole heads where possible),
-// keeping a head's K/V re-reads inside one XCD's L2.  Causal grids visit the
-// longest query tiles of a head first.
 // Work item of this workgroup.  The grid's items come in runs of per_head
 // (one head's tiles, heaviest first when the mask is causal).  Workgroups
 // are handed to the 8 XCDs round-robin (blockIdx % 8), and each XCD has its
@@ -101,9 +96,43 @@ __device__ __forceinline__ int xcd_item(int per_head) {
     return x * per + local;
 }
 
+// Work item of this workgroup on a causal grid, where the items of a head
+// differ in cost (query tile qt sees the keys of query tiles 0..qt).  The XCD shares
+// are those of xcd_item; within a share the order changes so that the
+// workgroups that share a CU carry balanced work.  Within an XCD the
+// dispatcher deals consecutive workgroups to its CUs in turn (observed with
+// the hardware ID registers: the XCD's workgroups l, l + 32, l + 64, ... land
+// on one CU), so the share's items are taken rank-major (the heaviest tile
+// of every head, then the next heaviest, ...) and dealt in a snake: round j
+// of kCusPerXcd workgroups runs forward for even j and backward for odd j,
+// so a CU that gets one of the heaviest items in one round gets one of the
+// lighter ones in the next.  For B8 H12 N1024 (one round of 768 workgroups,
+// three per CU) the work per CU goes from 6..48 key tiles to 24..30.  The
+// order is a permutation of the items for every grid; a final partial
+// round keeps its order.
+constexpr int kCusPerXcd = 32;
+
+__device__ __forceinline__ int xcd_item_causal(int per_head) {
+    const int G = gridDim.x;
+    const int id = blockIdx.x;
+    if ((G & 7) != 0) return id;
+    const int per = G >> 3, x = id & 7, local = id >> 3;
+    if (per_head > per || per % per_head != 0) return xcd_item(per_head);
+    const int heads = per / per_head;
+    const int j = local / kCusPerXcd, c = local - j * kCusPerXcd;
+    const bool reverse = (j & 1) && (j + 1) * kCusPerXcd <= per;
+    const int p = reverse ? j * kCusPerXcd + kCusPerXcd - 1 - c : local;
+    const int rank = p / heads, head = p - rank * heads;
+    return x * per + head * per_head + rank;
+}
+
+// Workgroup -> (head, query tile).  Causal grids take the longest query
+// tiles first, in the CU-balanced order of xcd_item_causal; other grids
+// take each head's tiles in order, whole heads per XCD where possible
+// (keeping a head's K/V re-reads inside one XCD's L2).
 __device__ __forceinline__ void tile_of_block(int nqt, bool longest_first,
                                               int *bh, int *qt) {
-    const int id = xcd_item(nqt);
+    const int id = longest_first ? xcd_item_causal(nqt) : xcd_item(nqt);
     *bh = id / nqt;
     const int r = id - *bh * nqt;
     *qt = longest_first ? nqt - 1 - r : r;
