@@ -160,10 +160,11 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 // Workgroup -> (query-head split, batch * key/value head, key block), via
 // the XCD-aware item order of xcd_item: the splits of one key block are
 // adjacent (they read the same K and V), and within a head the key blocks
-// run in ascending order (causal: the ones that see the most query rows
-// first).
-__device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt) {
-    int id = xcd_item(nkt * nsplit);
+// run in ascending order.  Causal grids, where key block kt is seen by the
+// query rows from kt on (the first blocks the most), use the CU-balanced
+// order of xcd_item_causal instead (heaviest blocks of every head first).
+__device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt, bool causal) {
+    int id = causal ? xcd_item_causal(nkt * nsplit) : xcd_item(nkt * nsplit);
     *split = id % nsplit;
     id /= nsplit;
     *bkv = id / nkt;
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     // Workgroup -> (batch, key/value head, key block, query-head split);
     // causal grids start with the key blocks that see the most query rows.
     int split, bkv, kt;
-    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt);
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + wave * 32;
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     const int N = a.N;
     const int nkt = (N + BK - 1) / BK;
     int split, bkv, kt;
-    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt);
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + kg * 32;
@@ -670,8 +671,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     const int N = a.N;
     const int nqt = (N + BR - 1) / BR;
     // (query tile, key-range split): the splits of one query tile adjacent,
-    // heads and tiles in the XCD-aware order, causal tiles longest first.
-    const int item = xcd_item(nqt * a.nsplit_q);
+    // heads and tiles in the XCD-aware order; causal grids longest first in
+    // the CU-balanced order.
+    const int item = CAUSAL ? xcd_item_causal(nqt * a.nsplit_q) : xcd_item(nqt * a.nsplit_q);
     const int split = item % a.nsplit_q;
     const int rest = item / a.nsplit_q;
     const int bh = rest / nqt;
