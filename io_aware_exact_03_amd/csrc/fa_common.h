@@ -97,20 +97,24 @@ __device__ __forceinline__ int xcd_item(int per_head) {
 }
 
 // Work item of this workgroup on a causal grid, where the items of a head
-// differ in cost (query tile qt sees the keys of query tiles 0..qt).  The
-// XCD shares are those of xcd_item; within a share the order changes so
-// that the workgroups that share a CU carry balanced work.  Within an XCD
-// the dispatcher deals consecutive workgroups to its CUs in turn (observed
-// with the hardware ID registers: the XCD's workgroups l, l + 32, l + 64, ...
-// land on one CU), so the share is dealt in a snake: round j of kCusPerXcd
-// workgroups runs forward for even j and backward for odd j, and a CU that
-// gets one of the heaviest items in one round gets one of the lighter ones
-// in the next.  Short heads are first taken rank-major (the heaviest item
-// of every head, then the next heaviest, ...), since one head's items do
-// not span the rounds.  For B8 H12 N1024 (one round of 768 workgroups,
-// three per CU) the work per CU goes from 6..48 key tiles to 24..30.  The
-// order is a permutation of the items for every grid; a final partial
-// round keeps its order.
+// differ in cost (query tile qt sees the keys of query tiles 0..qt).  The XCD shares
+// are those of xcd_item; within a share the order changes so that the
+// workgroups that share a CU carry balanced work.  Within an XCD the
+// dispatcher deals consecutive workgroups to its CUs in turn (observed with
+// the hardware ID registers: the XCD's workgroups l, l + 32, l + 64, ... land
+// on one CU), so the share's items are taken rank-major (the heaviest tile
+// of every head, then the next heaviest, ...) and dealt in a snake: round j
+// of kCusPerXcd workgroups runs forward for even j and backward for odd j,
+// so a CU that gets one of the heaviest items in one round gets one of the
+// lighter ones in the next.  For B8 H12 N1024 (one round of 768 workgroups,
+// three per CU) the work per CU goes from 6..48 key tiles to 24..30.  On
+// long grids the rank-major order is longest-first across all heads of the
+// XCD, which shortens the tail; it also keeps several heads' K/V streams in
+// the XCD's L2 at once, which raised the HBM fetches of B1 H16 N16384 d128
+// from 365 to 699 MB per launch (0.7 TB/s) while the time went down
+// (head-major within the snake measured 1 % slower there and 6 % slower
+// at d = 64).  The order is a permutation of the items for every grid; a
+// final partial round keeps its order.
 constexpr int kCusPerXcd = 32;
 
 __device__ __forceinline__ int xcd_item_causal(int per_head) {
@@ -123,11 +127,6 @@ __device__ __forceinline__ int xcd_item_causal(int per_head) {
     const int j = local / kCusPerXcd, c = local - j * kCusPerXcd;
     const bool reverse = (j & 1) && (j + 1) * kCusPerXcd <= per;
     const int p = reverse ? j * kCusPerXcd + kCusPerXcd - 1 - c : local;
-    // A head of 4 * kCusPerXcd items or more fills the CU rounds that are
-    // resident together by itself: it stays head-major, so the XCD's L2
-    // holds one head's K/V at a time (interleaving two 16K heads doubled the
-    // HBM traffic of B1 H16 N16384 d128, 365 -> 699 MB per launch).
-    if (per_head >= 4 * kCusPerXcd) return x * per + p;
     const int rank = p / heads, head = p - rank * heads;
     return x * per + head * per_head + rank;
 }
