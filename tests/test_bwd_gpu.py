@@ -70,6 +70,15 @@ def run_case(B, H, H_kv, N, d, seed, causal=False, key_len=None, block_mask=None
     return errs
 
 
+@pytest.mark.parametrize("B,H,N", [(4, 24, 512), (8, 16, 512), (1, 4, 2048), (2, 5, 1536), (1, 3, 640)])
+def test_bwd_causal_work_orders(B, H, N):
+    """Causal grids whose sizes select every branch of the CU-balanced work
+    order of the dK/dV and dQ kernels (a full round then a partial one, a
+    reversed round, a head over two XCDs, shares without whole heads, a grid
+    that is not a multiple of 8); gradients start as NaN."""
+    run_case(B, H, H, N, 64, seed=300 + N + H, causal=True)
+
+
 def modes(N, seed):
     rng = np.random.default_rng(seed)
     nb = (N + 127) // 128

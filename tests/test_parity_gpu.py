@@ -199,6 +199,23 @@ def test_very_long_sequences_sampled_rows(N, d, causal):
               f"N={N} tile study")
 
 
+# Causal grids whose work orders take every branch of the CU-balanced order.
+CAUSAL_ORDER_SHAPES = [(4, 24, 512),    # 48 items per XCD: a full round, then a partial one kept in order
+               (8, 16, 512),    # 64 per XCD: the second round dealt in reverse
+               (1, 4, 2048),    # one head spans two XCDs
+               (2, 5, 1536),    # 15 per XCD, heads of 12 items: shares do not hold whole heads
+               (1, 3, 640)]     # 15 workgroups, not a multiple of the 8 XCDs
+
+
+@pytest.mark.parametrize("B,H,N", CAUSAL_ORDER_SHAPES)
+def test_causal_work_orders(B, H, N):
+    """Every (head, query tile) of a causal grid is computed exactly once
+    whatever branch of the work order the grid size selects (outputs start
+    as NaN, so a tile left out shows)."""
+    inp = custom(B, H, N, 64, seed=97 + N + H, causal=True)
+    check(*run(inp), *ref(inp), TOL_BF16, f"B{B} H{H} N{N}")
+
+
 def _multi_chunk_mask(nb):
     """Block-mask rows of five kinds, cycling with the query block: active
     blocks only in the last 64-block chunk, only in the middle chunk, none,
