@@ -197,7 +197,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); "
               "the attention path shards over (batch, head) pairs with no communication",
               file=sys.stderr)
         sys.exit(2)
