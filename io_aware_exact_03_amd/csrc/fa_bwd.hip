@@ -164,7 +164,8 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 // query rows from kt on (the first blocks the most), use the CU-balanced
 // order of xcd_item_causal instead (heaviest blocks of every head first).
 __device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt, bool causal) {
-    int id = causal ? xcd_item_causal(nkt * nsplit) : xcd_item(nkt * nsplit);
+    // the causal dK/dV kernel (the pair kernel) fits one workgroup per CU
+    int id = causal ? xcd_item_causal(nkt * nsplit, 1) : xcd_item(nkt * nsplit);
     *split = id % nsplit;
     id /= nsplit;
     *bkv = id / nkt;
@@ -673,7 +674,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     // (query tile, key-range split): the splits of one query tile adjacent,
     // heads and tiles in the XCD-aware order; causal grids longest first in
     // the CU-balanced order.
-    const int item = CAUSAL ? xcd_item_causal(nqt * a.nsplit_q) : xcd_item(nqt * a.nsplit_q);
+    // two (d = 128) or three (d = 64) workgroups per CU
+    const int item = CAUSAL ? xcd_item_causal(nqt * a.nsplit_q, D == 128 ? 2 : 3) : xcd_item(nqt * a.nsplit_q);
     const int split = item % a.nsplit_q;
     const int rest = item / a.nsplit_q;
     const int bh = rest / nqt;

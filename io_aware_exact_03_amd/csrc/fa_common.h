@@ -97,47 +97,67 @@ __device__ __forceinline__ int xcd_item(int per_head) {
 }
 
 // Work item of this workgroup on a causal grid, where the items of a head
-// differ in cost (query tile qt sees the keys of query tiles 0..qt).  The XCD shares
-// are those of xcd_item; within a share the order changes so that the
-// workgroups that share a CU carry balanced work.  Within an XCD the
-// dispatcher deals consecutive workgroups to its CUs in turn (observed with
-// the hardware ID registers: the XCD's workgroups l, l + 32, l + 64, ... land
-// on one CU), so the share's items are taken rank-major (the heaviest tile
-// of every head, then the next heaviest, ...) and dealt in a snake: round j
-// of kCusPerXcd workgroups runs forward for even j and backward for odd j,
-// so a CU that gets one of the heaviest items in one round gets one of the
-// lighter ones in the next.  For B8 H12 N1024 (one round of 768 workgroups,
-// three per CU) the work per CU goes from 6..48 key tiles to 24..30.  On
-// long grids the rank-major order is longest-first across all heads of the
-// XCD, which shortens the tail; it also keeps several heads' K/V streams in
-// the XCD's L2 at once, which raised the HBM fetches of B1 H16 N16384 d128
-// from 365 to 699 MB per launch (0.7 TB/s) while the time went down
-// (head-major within the snake measured 1 % slower there and 6 % slower
-// at d = 64).  The order is a permutation of the items for every grid; a
-// final partial round keeps its order.
+// differ in cost (query tile qt sees the keys of query tiles 0..qt).  The
+// XCD shares are those of xcd_item; within a share the order changes so
+// that the workgroups that share a CU carry balanced work.  Within an XCD
+// the dispatcher deals consecutive workgroups to its CUs in turn (observed
+// with the hardware ID registers: the XCD's workgroups l, l + 32, l + 64, ...
+// land on one CU), so the rounds that are resident together, the first
+// `resident` rounds of kCusPerXcd workgroups (resident = workgroups of the
+// kernel that fit on a CU at once), are dealt in a snake: forward for even
+// rounds, backward for odd ones, so a CU that gets one of the heaviest
+// items in one round gets one of the lighter ones in the next.  Later
+// rounds are handed out as CUs free up and keep the heaviest-first order
+// (snaking them hands out light items first: the GQA-4 16K backward, one
+// dK/dV workgroup per CU, ran 17 % slower).  Where whole heads fit in a share they are first taken
+// rank-major (the heaviest item of every head, then the next heaviest,
+// ...); where a head spans X XCDs, its items stay round-robin over them as
+// in xcd_item and each XCD's part is snaked.  For B8 H12 N1024 (one round
+// of 768 workgroups, three per CU) the work per CU goes from 6..48 key
+// tiles to 24..30; for B1 H4 N16384 (512 workgroups, two per CU, each head
+// over two XCDs) from 68..192 to 130 tile units.  On long grids the
+// rank-major order is longest-first across all heads of the XCD, which
+// shortens the tail; it also keeps several heads' K/V streams in the XCD's
+// L2 at once, which raised the HBM fetches of B1 H16 N16384 d128 from 365
+// to 699 MB per launch (0.7 TB/s) while the time went down (head-major
+// within the snake measured 1 % slower there and 6 % slower at d = 64).
+// The order is a permutation of the items for every grid; a final partial
+// round keeps its order.
 constexpr int kCusPerXcd = 32;
 
-__device__ __forceinline__ int xcd_item_causal(int per_head) {
+__device__ __forceinline__ int snake_local(int local, int per, int resident) {
+    const int j = local / kCusPerXcd, c = local - j * kCusPerXcd;
+    const bool reverse = (j & 1) && j < resident && (j + 1) * kCusPerXcd <= per;
+    return reverse ? j * kCusPerXcd + kCusPerXcd - 1 - c : local;
+}
+
+__device__ __forceinline__ int xcd_item_causal(int per_head, int resident) {
     const int G = gridDim.x;
     const int id = blockIdx.x;
     if ((G & 7) != 0) return id;
     const int per = G >> 3, x = id & 7, local = id >> 3;
-    if (per_head > per || per % per_head != 0) return xcd_item(per_head);
-    const int heads = per / per_head;
-    const int j = local / kCusPerXcd, c = local - j * kCusPerXcd;
-    const bool reverse = (j & 1) && (j + 1) * kCusPerXcd <= per;
-    const int p = reverse ? j * kCusPerXcd + kCusPerXcd - 1 - c : local;
-    const int rank = p / heads, head = p - rank * heads;
-    return x * per + head * per_head + rank;
+    const int p = snake_local(local, per, resident);
+    if (per_head > per && per_head % per == 0) {
+        // a head spans X XCDs, which take its items round-robin (xcd_item)
+        const int X = per_head / per;
+        const int head = x / X, j = x - head * X;
+        return head * per_head + j + X * p;
+    }
+    if (per % per_head == 0) {
+        const int heads = per / per_head;
+        const int rank = p / heads, head = p - rank * heads;
+        return x * per + head * per_head + rank;
+    }
+    return x * per + p;
 }
 
 // Workgroup -> (head, query tile).  Causal grids take the longest query
 // tiles first, in the CU-balanced order of xcd_item_causal; other grids
 // take each head's tiles in order, whole heads per XCD where possible
 // (keeping a head's K/V re-reads inside one XCD's L2).
-__device__ __forceinline__ void tile_of_block(int nqt, bool longest_first,
+__device__ __forceinline__ void tile_of_block(int nqt, bool longest_first, int resident,
                                               int *bh, int *qt) {
-    const int id = longest_first ? xcd_item_causal(nqt) : xcd_item(nqt);
+    const int id = longest_first ? xcd_item_causal(nqt, resident) : xcd_item(nqt);
     *bh = id / nqt;
     const int r = id - *bh * nqt;
     *qt = longest_first ? nqt - 1 - r : r;

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(NW * 64, (MF == 32 && NW == 4) ? 2 : 1) void fwd_bf
     const int N = a.N;
     const int nqt = (N + C::BR - 1) / C::BR;
     int bh, qt;
-    tile_of_block(nqt, CAUSAL, &bh, &qt);
+    tile_of_block(nqt, CAUSAL, 1, &bh, &qt);
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;

@@ -139,7 +139,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
         const int r = rest - bh * nqt;
         qt = CAUSAL ? nqt - 1 - r : r;
     } else {
-        tile_of_block(nqt, CAUSAL, &bh, &qt);
+        // workgroups resident per CU: 2 at d = 128 and 3 at d = 64 with 4
+        // waves (218 and 156 registers), 1 with 8 waves
+        tile_of_block(nqt, CAUSAL, NW == 4 ? (D == 128 ? 2 : 3) : 1, &bh, &qt);
     }
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kNwF32 * 64) void fwd_f32_kernel(FwdArgs a) {
     const int N = a.N;
     const int nqt = (N + BR - 1) / BR;
     int bh, qt;
-    tile_of_block(nqt, CAUSAL, &bh, &qt);
+    tile_of_block(nqt, CAUSAL, 1, &bh, &qt);
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
