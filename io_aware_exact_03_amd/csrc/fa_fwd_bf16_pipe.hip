@@ -131,8 +131,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     int bh, qt, split = 0;
     if constexpr (SPLIT) {
         // (query tile, key-range share): the shares of one query tile are
-        // adjacent items; heads and tiles in the usual XCD-aware order.
-        const int item = xcd_item(nqt * a.nsplit);
+        // adjacent items; heads and tiles in the usual XCD-aware order, at
+        // d = 128 causal in the CU-balanced order (2 resident workgroups per
+        // CU: B1 H1 N32768 333 -> 313 us, B2 H2 N8192 109 -> 105 us; at
+        // d = 64 it measured 1-2 % slower and is not used).
+        const int item = CAUSAL && D == 128 ? xcd_item_causal(nqt * a.nsplit, 2) : xcd_item(nqt * a.nsplit);
         split = item % a.nsplit;
         const int rest = item / a.nsplit;
         bh = rest / nqt;
