@@ -15,13 +15,21 @@ Prints ONE JSON line:
               separate pass after the timed region);
               traffic = measured HBM bytes per launch from the committed
               rocprofv3 counter summary if it was taken on the current
-              kernel sources, else null; likewise sclk_ghz, the shader clock
-              the kernel ran at in that counter run (GPU-busy cycles per
-              XCD over the dispatch time), with the matrix-core peak at that
-              clock (256 CUs x sclk x 4096 FLOP/clk) and the fraction of it
+              kernel sources, else null
+  power       board power, shader clock and energy per launch, sampled
+              through the SMI library over a loop of back-to-back launches
+              of at least 2 s after the timed region (this run, this GPU);
+              sclk_ghz / peak_at_sclk / frac_at_sclk in the roofline object
+              come from it and are diagnostic only: roofline.frac against the
+              2.4 GHz peak is the figure compared with the target
   cpu_baseline the FP64 oracle timed on the host cores on a bounded sample
               of query rows of the same workload, in the same unit; the
               GPU/oracle deviation on those rows is reported beside it
+  tile_sweep  (16K causal workload only) the deviation study on rows
+              0..2047 of heads 0..3: max|dO| and max|dLSE| against the FP64
+              oracle for every (Br, Bc) in {16, 32, 64, 128}^2
+  n_curve     TFLOP/s and fraction of the bf16 peak at N = 1K..16K (16 heads,
+              B = 16384/N, d = 64 and 128, causal and not)
 """
 import argparse
 import hashlib
@@ -70,20 +78,114 @@ def measured_traffic(workload):
     return _profiled(workload, "bytes_per_launch")
 
 
-def measured_sclk(workload):
-    """Shader clock (GHz) of the counter run: GRBM_GUI_ACTIVE / 8 XCDs over
-    the dispatch time."""
-    return _profiled(workload, "sclk_ghz")
-
-
-def sclk_fields(achieved, workload, dtype):
-    """The matrix-core peak at the profiled shader clock, and the fraction
-    of it reached (bf16 only; None when no valid counter run exists)."""
-    ghz = measured_sclk(workload) if dtype == "bf16" else None
+def sclk_fields(achieved, power, dtype):
+    """The matrix-core peak at the shader clock measured in this run (the
+    power loop's average over the XCDs), and the fraction of it reached.
+    Diagnostic only; None when no clock reading exists."""
+    ghz = power.get("gfx_clock_ghz") if power and dtype == "bf16" else None
     if not ghz:
         return {"sclk_ghz": None, "peak_at_sclk": None, "frac_at_sclk": None}
     peak = BF16_FLOP_PER_CLK * ghz * 1e9 / 1e12
     return {"sclk_ghz": round(ghz, 3), "peak_at_sclk": round(peak, 1), "frac_at_sclk": round(achieved / peak, 4)}
+
+
+def _smi_handle(torch):
+    """SMI handle of the GPU torch calls cuda:0 (matched by PCI bus), or the
+    only GPU the SMI library sees."""
+    import amdsmi
+    amdsmi.amdsmi_init()
+    handles = amdsmi.amdsmi_get_processor_handles()
+    if not handles:
+        raise RuntimeError("SMI sees no GPU")
+    props = torch.cuda.get_device_properties(0)
+    bus = getattr(props, "pci_bus_id", None)
+    for h in handles:
+        try:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+            if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                return amdsmi, h
+        except Exception:
+            pass
+    if len(handles) == 1:
+        return amdsmi, handles[0]
+    raise RuntimeError(f"cannot match cuda:0 (bus {bus}) among {len(handles)} SMI GPUs")
+
+
+def power_loop(torch, step, seconds=2.0, period=0.02):
+    """Back-to-back launches for at least `seconds` while a thread samples the
+    SMI metrics every `period` s: board power, the shader clock of each XCD,
+    the power limit, throttle status and the energy counter.  Returns a dict
+    (or {"error": ...} when the SMI library is unavailable)."""
+    import threading
+    try:
+        amdsmi, h = _smi_handle(torch)
+    except Exception as e:  # no SMI access: reported, never fatal
+        return {"error": f"{type(e).__name__}: {e}"}
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+                samples.append(dict(t=time.perf_counter(), power=m.get("current_socket_power"),
+                                    clk=sum(clks) / len(clks) if clks else m.get("current_gfxclk"),
+                                    clk_min=min(clks) if clks else None,
+                                    throttle=m.get("throttle_status"),
+                                    hotspot=m.get("temperature_hotspot")))
+            except Exception:
+                pass
+            stop.wait(period)
+
+    def energy():
+        e = amdsmi.amdsmi_get_energy_count(h)
+        return e["energy_accumulator"] * e["counter_resolution"] * 1e-6  # joules
+
+    try:
+        limit = amdsmi.amdsmi_get_power_info(h).get("power_limit")
+    except Exception:
+        limit = None
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(3 * period)
+    e0 = energy()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    t1 = time.perf_counter()
+    e1 = energy()
+    stop.set()
+    th.join()
+    busy = [x for x in samples if t0 + 0.1 <= x["t"] <= t1]
+    num = lambda key: [x[key] for x in busy if isinstance(x[key], (int, float))]
+    mean = lambda v: sum(v) / len(v) if v else None
+    pw, clk, cmin = num("power"), num("clk"), num("clk_min")
+    joules = e1 - e0
+    out = {
+        "loop_s": round(t1 - t0, 3), "launches": n, "samples": len(busy),
+        "board_power_w_avg": round(mean(pw), 1) if pw else None,
+        "board_power_w_max": max(pw) if pw else None,
+        "power_limit_w": limit,
+        "gfx_clock_ghz": round(mean(clk) / 1000.0, 4) if clk else None,
+        "gfx_clock_ghz_min_xcd": round(min(cmin) / 1000.0, 4) if cmin else None,
+        "energy_j_per_launch": round(joules / n, 6) if n else None,
+        "avg_power_from_energy_w": round(joules / (t1 - t0), 1),
+        "throttle_status_seen": sorted({x["throttle"] for x in busy if x["throttle"] not in (None, "N/A")}),
+        "hotspot_c_max": max(num("hotspot")) if num("hotspot") else None,
+    }
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    return out
 
 
 def algorithmic_bytes(w, inp):
@@ -179,6 +281,10 @@ def main():
     ap.add_argument("--bc", type=int, default=0, help="key rows per tile (0 = tuned)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for the CPU baseline (0 = skip)")
+    ap.add_argument("--power-seconds", type=float, default=2.0,
+                    help="length of the SMI power/clock loop after the timed region (0 = skip)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the tile sweep and the sequence-length curve")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (3 times), the known-size "
                          "reference that scales the FETCH_SIZE/WRITE_SIZE counters")
@@ -260,6 +366,8 @@ def main():
             return float("nan")
         return launch_ms[min(len(launch_ms) - 1, int(round(p / 100 * (len(launch_ms) - 1))))]
 
+    power = power_loop(torch, step, args.power_seconds) if args.power_seconds > 0 else None
+
     pairs = allowed_pairs(w.N, w.B, w.H, w.causal, inp["key_len"], inp["block_mask"])
     flop = 4 * w.d * pairs
     value = flop / (wall_ms * 1e-3) / 1e12
@@ -294,15 +402,77 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.key),
-                     **sclk_fields(achieved, w.key, w.dtype),
+                     **sclk_fields(achieved, power, w.dtype),
                      "kernel_ms": round(kern_ms, 5),
                      "launch_ms_p10_p50_p90": [round(pct(10), 5), round(pct(50), 5), round(pct(90), 5)],
                      "algorithmic_bytes": algorithmic_bytes(w, inp)},
         "cpu_baseline": cpu,
         "max_abs_dO_sampled": dev_o,
         "max_abs_dLSE_sampled": dev_l,
+        "power": power,
     }
+    if not args.no_extras:
+        if w.key == "long_causal":
+            line["tile_sweep"] = tile_sweep(torch, fa, w)
+        line["n_curve"] = n_curve(torch, fa)
     print(json.dumps(line), flush=True)
+
+
+def tile_sweep(torch, fa, w):
+    """Deviation study of the 16K causal workload: rows 0..2047 of heads 0..3
+    (a self-contained causal problem), every (Br, Bc) in {16, 32, 64, 128}^2
+    on the tile-study kernels plus the tuned default, max|dO| and max|dLSE|
+    against the FP64 oracle."""
+    import numpy as np
+    import oracle
+    from workloads import causal_prefix
+    inp = causal_prefix(w, N=2048, H=4)
+    o_ref, lse_ref = oracle.attention_f64(inp["q"], inp["k"], inp["v"], float(inp["scale"]), True)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    rows = []
+    for br, bc in [(0, 0)] + [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128)]:
+        o, lse = fa.fwd(q, k, v, causal=True, scale=float(inp["scale"]), Br=br, Bc=bc)
+        torch.cuda.synchronize()
+        do = np.abs(o.double().cpu().numpy() - o_ref)
+        dl = np.abs(lse.double().cpu().numpy() - lse_ref)
+        rows.append({"br": br or 128, "bc": bc or 64, "kernel": "tuned" if br == 0 else "tile-study",
+                     "max_dO": float(do.max()), "mean_dO": float(do.mean()), "max_dLSE": float(dl.max())})
+    return {"slice": "B1 H4 N2048 d128 causal (rows 0..2047 of heads 0..3)", "rows": rows}
+
+
+def n_curve(torch, fa, launches=20):
+    """Median-of-launches TFLOP/s at N = 1K..16K, 16 heads, B = 16384/N,
+    d = 64 and 128, causal and not; N(0,1) bf16 inputs drawn on the GPU from
+    a seeded generator (seed 2000 + log2 N)."""
+    dev = torch.device("cuda:0")
+    out = []
+    for d in (64, 128):
+        for N in (1024, 2048, 4096, 8192, 16384):
+            B, H = 16384 // N, 16
+            g = torch.Generator(device=dev)
+            g.manual_seed(2000 + int(math.log2(N)))
+            q, k, v = (torch.randn((B, H, N, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+            for causal in (False, True):
+                for _ in range(5):
+                    fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(launches)]
+                st = torch.cuda.current_stream()
+                for e0, e1 in ev:
+                    e0.record(st)
+                    fa.fwd(q, k, v, causal=causal, out=o, lse=lse)
+                    e1.record(st)
+                torch.cuda.synchronize()
+                ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[launches // 2]
+                pairs = B * H * (N * (N + 1) // 2 if causal else N * N)
+                tf = 4 * d * pairs / (ms * 1e-3) / 1e12
+                out.append({"N": N, "B": B, "d": d, "causal": causal, "us": round(ms * 1e3, 2),
+                            "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+            del q, k, v, o, lse
+    return out
 
 
 if __name__ == "__main__":

@@ -34,7 +34,8 @@
  *                16-byte aligned; owned by the caller.  o must not overlap
  *                q, k or v.
  *   lse        : DEVICE pointer to float [B, H, N] (4-byte aligned) or NULL
- *                (then no logsumexp is written).
+ *                (then no logsumexp is written); must not overlap q, k, v
+ *                or o.
  *   key_len    : DEVICE pointer to int32 [B] or NULL.
  *   block_mask : DEVICE pointer to uint8 [nb * nb] or NULL; row = query
  *                block, column = key block, 128 x 128 tokens per block.
@@ -73,8 +74,8 @@ typedef enum {
     FA_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte, lse/key_len not 4-byte */
     FA_ERR_UNSUPPORTED_TILE = 5,     /* (Br, Bc) pair or dtype not built            */
     FA_ERR_HIP = 6,                  /* the kernel launch failed                    */
-    FA_ERR_INVALID_ARG = 7           /* non-finite scale, o overlapping an input,
-                                        unknown tile order                          */
+    FA_ERR_INVALID_ARG = 7           /* non-finite scale, o or lse overlapping an
+                                        input or each other, unknown tile order     */
 } fa_status;
 
 /* Element type codes for fa_fwd_ex and fa_fwd_gqa.  FA_DTYPE_F16 (IEEE
@@ -98,7 +99,10 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 
 /*
  * fp32 inputs and output, fp32 arithmetic throughout (fp32 matrix-core
- * products).  Same arguments and semantics as fa_fwd.
+ * products, probabilities never rounded to a 16-bit type).  Same arguments
+ * and semantics as fa_fwd.  This is the higher-precision end of the precision
+ * axis that the page "Is Flash Attention Stable?" explainer (aibr.jp,
+ * section 3) sets against BF16, each compared with an FP64 golden value.
  */
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
                float *lse, int B, int H, int N, int d, float scale, int causal,
@@ -268,10 +272,17 @@ size_t fa_bwd_workspace_size(int B, int H, int H_kv, int N, int d);
 int fa_tile_shape(int dtype, int d, int block_sparse, int Br, int Bc,
                   int *br_out, int *bc_out);
 
-/* Static text for a status code; unknown codes give "unknown status". */
+/* Error reporting.  The page "Is Flash Attention Stable?" explainer (aibr.jp,
+ * section 6) asks attention libraries to expose their settings and to carry
+ * hooks for detecting errors; every entry point above returns a status code,
+ * and these two calls explain it. */
+
+/* Static text for a status code; unknown codes give "unknown status".  Never
+ * NULL; the string is owned by the library. */
 const char *fa_status_string(int status);
 
-/* hipError_t of the most recent FA_ERR_HIP on the calling thread (0 if none). */
+/* hipError_t of the most recent FA_ERR_HIP on the calling thread (0 if none).
+ * A thread-local value: calls on other threads do not change it. */
 int fa_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -78,9 +78,17 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     const uint64_t elem = dtype == FA_DTYPE_F32 ? 4 : 2;
     const uint64_t bytes = (uint64_t)B * H * N * d * elem;
     const uint64_t kv_bytes = (uint64_t)B * Hkv * N * d * elem;
-    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, kv_bytes) || overlaps(o, bytes, v, kv_bytes))
-        return FA_ERR_INVALID_ARG;
+    // Outputs (o, and lse when given) must not overlap any input or each
+    // other: a workgroup writing them while others still read the inputs
+    // would corrupt the result silently.
     const uint64_t lse_bytes = (uint64_t)B * H * N * sizeof(float);
+    const struct { const void *p; uint64_t n; } ins[] = {{q, bytes}, {k, kv_bytes}, {v, kv_bytes}};
+    const struct { const void *p; uint64_t n; } outs[] = {{o, bytes}, {lse, lse ? lse_bytes : 0}};
+    for (const auto &w : outs) {
+        if (!w.p) continue;
+        for (const auto &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
+    }
     if (lse && overlaps(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
 
     if (order != FA_ORDER_ASCENDING && order != FA_ORDER_DESCENDING && order != FA_ORDER_SHUFFLED)

@@ -34,7 +34,7 @@
  *
  * Layout: q, o are contiguous [B, H, N, d]; k, v are [B, H, N, d] (or
  * [B, Hkv, N, d] for the grouped-query entry points); lse is [B, H, N].
- * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/build.py).
+ * Build: gcc -O3 -march=native -std=c11 -fopenmp -shared -fPIC (oracle/build.py).
  */
 #include <math.h>
 #include <stdint.h>

@@ -65,6 +65,9 @@ def call(**kw):
     (dict(Br=256, Bc=64, block_mask=0x70000000), 5),
     (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
     (dict(o=Q + 64), 7), (dict(lse=O + 16), 7), (dict(lse=O - 2 * 3 * 100 * 4 + 4), 7),
+    # lse over an input: the kernel would write it while other workgroups read
+    (dict(lse=Q + 4), 7), (dict(lse=K + 2 * 3 * 100 * 64 * 2 - 4), 7), (dict(lse=V - 2 * 3 * 100 * 4 + 4), 7),
+    (dict(lse=K), 7),
 ])
 def test_invalid_arguments_return_status_without_launch(kw, status):
     assert call(**kw) == status

@@ -181,6 +181,64 @@ def test_large_workloads_sampled_rows(name):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
+@pytest.mark.parametrize("name", ["long_causal", "block_sparse"])
+def test_large_workloads_full(name):
+    """Every row of O and LSE of the two long workloads (16K causal d = 128;
+    4K block-sparse d = 64 with its seeded mask) against the full FP64
+    oracle, on the same launch configuration the benchmark times."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    o, lse = run(inp)
+    o_ref, lse_ref = ref(inp)
+    err = check(o, lse, o_ref, lse_ref, TOL_BF16, name)
+    fin = np.isfinite(lse_ref)
+    print(f"{name}: full comparison over {o.size} outputs: max|dO| = {err:.3e}, "
+          f"max|dLSE| = {np.abs(lse[fin] - lse_ref[fin]).max():.3e}", flush=True)
+    assert fin.all(), "every row of these workloads sees at least one key"
+
+
+def _raw_call(entry, inp, dtype, lse_on=True):
+    """Calls a named C entry point directly (pointers and sizes only)."""
+    q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    kl = torch.from_numpy(inp["key_len"]).cuda() if inp.get("key_len") is not None else None
+    bm = torch.from_numpy(inp["block_mask"]).cuda() if inp.get("block_mask") is not None else None
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse_on else None,
+            B, H, N, d, float(inp["scale"]), bool(inp["causal"]),
+            kl.data_ptr() if kl is not None else None, bm.data_ptr() if bm is not None else None, stream]
+    if entry == "fa_fwd_ex":
+        fa.fa_fwd_ex(*args, fa.DTYPE_F32 if dtype == "f32" else fa.DTYPE_BF16, 0, 0)
+    else:
+        getattr(fa, entry)(*args)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("dtype,entry", [("bf16", "fa_fwd"), ("f32", "fa_fwd_f32")])
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_named_entry_points(dtype, entry, mode, d):
+    """fa_fwd and fa_fwd_f32 themselves: within the bar of the oracle and
+    bit-identical to fa_fwd_ex with the default tile."""
+    N = 300
+    inp = custom(2, 3, N, d, seed=700 + d, dtype=dtype, **modes_for(N, 701)[mode])
+    o, lse = _raw_call(entry, inp, dtype)
+    o_ex, lse_ex = _raw_call("fa_fwd_ex", inp, dtype)
+    assert torch.equal(o.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       o_ex.view(torch.int16 if dtype == "bf16" else torch.int32)), entry
+    assert torch.equal(lse.view(torch.int32), lse_ex.view(torch.int32)), entry
+    check(o.double().numpy(), lse.double().numpy(), *ref(inp), TOL_BF16 if dtype == "bf16" else TOL_F32,
+          f"{entry} d={d} {mode}")
+    # lse = NULL: O is unchanged and the LSE buffer is left as it was
+    o2, lse2 = _raw_call(entry, inp, dtype, lse_on=False)
+    assert torch.equal(o2.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       o.view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.isnan(lse2).all()
+
+
 @pytest.mark.parametrize("N,d,causal", [(65536, 128, True), (65533, 64, False), (40000, 128, True)])
 def test_very_long_sequences_sampled_rows(N, d, causal):
     """Single-head sequences up to 64K tokens (the longest context the
