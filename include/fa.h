@@ -202,6 +202,39 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
  * or the arguments are invalid).  Independent of H_kv, masks and scale. */
 size_t fa_fwd_workspace_size(int B, int H, int N, int d, int dtype);
 
+/* Size of the library's static scratch (fa_fwd_noalloc): the largest
+ * workspace fa_fwd_workspace_size returns for any shape.  A split is only
+ * used on grids of fewer than 512 query tiles, with at most 1024 shares in
+ * all, so its partials cover at most 1024 * 128 rows of d + 1 <= 129 floats. */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)1024 * 128 * 129 * 4)
+
+/*
+ * fa_fwd_ws for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation as fa_fwd_ws given the workspace fa_fwd_workspace_size
+ * asks for (identical bits), with the key-range split's fp32 partials kept
+ * in a static device array of FA_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library instead of a caller workspace.
+ *   Arguments, layouts, status codes: as fa_fwd_ws without the workspace
+ *   arguments.  The device is the current HIP device of the calling thread
+ *   (stream must belong to it).
+ *   Memory: the call allocates nothing.  The static array exists once per
+ *   GPU the library runs on and is held until the process ends; its address
+ *   on a device is looked up on the first call there (hipGetSymbolAddress).
+ *   A shape whose split would need more than FA_NOALLOC_SCRATCH_BYTES returns
+ *   FA_ERR_INVALID_SHAPE (no valid shape does: the constant is the largest
+ *   split workspace).
+ *   Concurrency: every call on one GPU uses that GPU's array.  Calls whose
+ *   work overlaps in time on one GPU (different streams, or different host
+ *   threads without ordering) race on it and may return wrong results; calls
+ *   ordered on one stream do not.  Nothing in the array has to start at
+ *   zero: every partial is written before it is read.
+ */
+int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int H_kv, int N, int d, float scale, int causal,
+                   const int32_t *key_len, const uint8_t *block_mask,
+                   hipStream_t stream, int dtype);
+
 /*
  * Backward pass: the gradients of the loss sum(dout * o) with respect to q,
  * k and v, for bf16 attention computed by fa_fwd / fa_fwd_gqa with the same

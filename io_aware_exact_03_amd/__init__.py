@@ -2,7 +2,7 @@
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
 ``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_fwd_ws``, ``fa_fwd_workspace_size``,
-``fa_bwd``, ``fa_bwd_ex``, ``fa_bwd_workspace_size``, ``fa_tile_shape``,
+``fa_fwd_noalloc``, ``fa_bwd``, ``fa_bwd_ex``, ``fa_bwd_workspace_size``, ``fa_tile_shape``,
 ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
@@ -14,7 +14,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size", "fa_bwd", "fa_bwd_ex",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size",
+           "fa_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_bwd", "fa_bwd_ex",
            "fa_bwd_workspace_size", "bwd",
            "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING", "ORDER_SHUFFLED",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
@@ -28,6 +29,8 @@ ORDER_ASCENDING = 0
 ORDER_DESCENDING = 1
 ORDER_SHUFFLED = 2
 MASK_BLOCK = 128
+# FA_NOALLOC_SCRATCH_BYTES of include/fa.h: the static scratch of fa_fwd_noalloc
+NOALLOC_SCRATCH_BYTES = 1024 * 128 * 129 * 4
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_INVALID_SHAPE",
@@ -81,6 +84,8 @@ def _load():
     lib.fa_fwd_ws.argtypes = [vp] * 5 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp, i32, vp,
                                                      ctypes.c_size_t]
     lib.fa_fwd_ws.restype = i32
+    lib.fa_fwd_noalloc.argtypes = [vp] * 5 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp, i32]
+    lib.fa_fwd_noalloc.restype = i32
     lib.fa_fwd_workspace_size.argtypes = [i32] * 5
     lib.fa_fwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -151,6 +156,12 @@ def fa_fwd_ws(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_m
                              block_mask, stream, dtype, workspace, workspace_bytes), "fa_fwd_ws")
 
 
+def fa_fwd_noalloc(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
+                   dtype):
+    _check(_load().fa_fwd_noalloc(q, k, v, o, lse, B, H, H_kv, N, d, scale, int(bool(causal)), key_len,
+                                  block_mask, stream, dtype), "fa_fwd_noalloc")
+
+
 def fa_fwd_workspace_size(B, H, N, d, dtype):
     return int(_load().fa_fwd_workspace_size(B, H, N, d, dtype))
 
@@ -193,7 +204,8 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
     permutation (tile-study kernels only).  ``workspace`` (tuned tile only):
     True allocates the key-range split workspace ``fa_fwd_workspace_size``
     asks for (grids too small for the GPU), a uint8 cuda tensor is used as
-    it, None (the default) runs unsplit.
+    it, "static" uses the library's own static scratch (fa_fwd_noalloc,
+    nothing allocated), None (the default) runs unsplit.
     """
     import torch
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -233,7 +245,13 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
         bm_ptr = block_mask.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    if workspace is not None and workspace is not False:
+    if isinstance(workspace, str):
+        if workspace != "static" or tile_order != ORDER_ASCENDING or Br or Bc:
+            raise ValueError('workspace="static" applies to the tuned tile in ascending order')
+        fa_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse.data_ptr() if want_lse else None, B, H, H_kv, N, d, float(scale),
+                       causal, kl_ptr, bm_ptr, stream, dtype)
+    elif workspace is not None and workspace is not False:
         if tile_order != ORDER_ASCENDING or Br or Bc:
             raise ValueError("the split workspace applies to the tuned tile in ascending order")
         if workspace is True:

@@ -6,11 +6,46 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa_internal.h"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Static scratch of fa_fwd_noalloc: the key-range split's fp32 partials
+// (partial O, then partial LSE), one copy per GPU, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// array: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+__device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there), or 0 with the HIP error in *err.
+uintptr_t scratch_on_current_device(hipError_t *err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return 0;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return 0;
+    }
+    uintptr_t p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *addr = nullptr;
+    *err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !addr) {
+        if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+        return 0;
+    }
+    // Concurrent first calls store the same address.
+    g_scratch_addr[dev].store(reinterpret_cast<uintptr_t>(addr), std::memory_order_release);
+    return reinterpret_cast<uintptr_t>(addr);
+}
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -62,7 +97,8 @@ int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
 int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
             int Hkv, int N, int d, float scale, int causal, const int32_t *key_len,
             const uint8_t *block_mask, hipStream_t stream, int dtype, int br, int bc,
-            int order = FA_ORDER_ASCENDING, void *workspace = nullptr, size_t workspace_bytes = 0) {
+            int order = FA_ORDER_ASCENDING, void *workspace = nullptr, size_t workspace_bytes = 0,
+            bool static_scratch = false) {
     if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
     if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -101,8 +137,21 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     if (rc != FA_OK) return rc;
     if (order != FA_ORDER_ASCENDING && !study) return FA_ERR_UNSUPPORTED_TILE;
     // Key-range split (fa_fwd_ws): used when a workspace is given and the
-    // shape gains from it; bf16/fp16 with the tuned tile only.
+    // shape gains from it; bf16/fp16 with the tuned tile only.  With the
+    // static scratch (fa_fwd_noalloc) the workspace is the library's own
+    // array, looked up only now that every argument has been checked.
     const uint64_t need = fa::fwd_workspace_bytes(B, H, N, d);
+    if (static_scratch && need > 0 && dtype != FA_DTYPE_F32) {
+        if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_INVALID_SHAPE;
+        hipError_t e = hipSuccess;
+        const uintptr_t p = scratch_on_current_device(&e);
+        if (!p) {
+            g_last_hip_error = (int)e;
+            return FA_ERR_HIP;
+        }
+        workspace = reinterpret_cast<void *>(p);
+        workspace_bytes = FA_NOALLOC_SCRATCH_BYTES;
+    }
     const bool split = workspace && need > 0 && dtype != FA_DTYPE_F32;
     if (split) {
         if (workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
@@ -253,6 +302,13 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, 
               size_t workspace_bytes) {
     return forward(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
                    dtype, 0, 0, FA_ORDER_ASCENDING, workspace, workspace_bytes);
+}
+
+int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                   int H_kv, int N, int d, float scale, int causal, const int32_t *key_len,
+                   const uint8_t *block_mask, hipStream_t stream, int dtype) {
+    return forward(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, block_mask, stream,
+                   dtype, 0, 0, FA_ORDER_ASCENDING, nullptr, 0, true);
 }
 
 size_t fa_fwd_workspace_size(int B, int H, int N, int d, int dtype) {

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study",
-                                           "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size", "fa_bwd", "fa_bwd_ex",
+                                           "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size",
+                                           "fa_fwd_noalloc", "fa_bwd", "fa_bwd_ex",
                                            "fa_bwd_workspace_size", "fa_tile_shape",
                                            "fa_status_string", "fa_last_hip_error"])
 
@@ -268,3 +269,36 @@ def test_fwd_workspace_validation(ws, nbytes, status):
     rc = lib.fa_fwd_ws(Q, K, V, O, LSE, 2, 3, 3, 100, 64, 0.125, 0, None, None, None, fa.DTYPE_BF16,
                        ws, nbytes)
     assert rc == status
+
+
+def test_noalloc_scratch_covers_every_split_workspace():
+    """The static scratch of fa_fwd_noalloc is the largest workspace the
+    key-range split asks for: splits run only on grids of fewer than 512
+    query tiles of 128 rows, with at most 1024 shares in all."""
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) \* (\d+) \* (\d+) \* (\d+)\)", text)
+    assert m, "FA_NOALLOC_SCRATCH_BYTES not found"
+    limit = math.prod(int(x) for x in m.groups())
+    assert limit == fa.NOALLOC_SCRATCH_BYTES
+    worst = 0
+    for d in (64, 128):
+        for B in (1, 2, 3, 4, 8):
+            for H in (1, 2, 3, 4, 6, 16):
+                for N in (1, 100, 127, 128, 129, 1000, 4096, 8191, 16384, 32768, 40000, 65536):
+                    need = fa.fa_fwd_workspace_size(B, H, N, d, fa.DTYPE_BF16)
+                    assert need <= limit, (B, H, N, d, need)
+                    worst = max(worst, need)
+    assert worst == limit  # reached by B1 H2 N16384 d128 (4 shares of 32768 rows)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(H_kv=3), 2), (dict(N=0), 2), (dict(d=96), 3), (dict(o=O + 2), 4),
+    (dict(scale=math.nan), 7), (dict(o=Q + 64), 7), (dict(lse=K + 16), 7), (dict(dtype=5), 5),
+])
+def test_noalloc_invalid_arguments_return_status_without_launch(kw, status):
+    args = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=2, H_kv=2, N=16384, d=128, scale=0.125, causal=1,
+                key_len=None, block_mask=None, stream=None, dtype=0)
+    args.update(kw)
+    names = ("q", "k", "v", "o", "lse", "B", "H", "H_kv", "N", "d", "scale", "causal", "key_len",
+             "block_mask", "stream", "dtype")
+    assert fa._load().fa_fwd_noalloc(*[args[n] for n in names]) == status
