@@ -26,8 +26,13 @@ Prints ONE JSON line:
               of query rows of the same workload, in the same unit; the
               GPU/oracle deviation on those rows is reported beside it
   tile_sweep  (16K causal workload only) the deviation study on rows
-              0..2047 of heads 0..3: max|dO| and max|dLSE| against the FP64
-              oracle for every (Br, Bc) in {16, 32, 64, 128}^2
+              0..2047 of heads 0..3: max|dO|, mean|dO| and max|dLSE| against
+              the FP64 oracle for every (Br, Bc) in {16, 32, 64, 128}^2 at
+              three precisions (bf16 O, bf16 inputs with O left in fp32, fp32),
+              non-ascending key-tile orders, and the materialised baseline
+  baseline_attention  time of the materialised baseline (S, then A, in
+              device memory) on the same workload, and the tiled kernel's
+              speed-up over it
   n_curve     TFLOP/s and fraction of the bf16 peak at N = 1K..16K (16 heads,
               B = 16384/N, d = 64 and 128, causal and not)
 """
@@ -413,32 +418,116 @@ def main():
     }
     if not args.no_extras:
         if w.key == "long_causal":
-            line["tile_sweep"] = tile_sweep(torch, fa, w)
+            line["tile_sweep"] = deviation_study(torch, fa, "long_causal", 2048, 4)
+        if w.dtype == "bf16":
+            line["baseline_attention"] = baseline_speed(torch, fa, w, inp, kern_ms)
         line["n_curve"] = n_curve(torch, fa)
     print(json.dumps(line), flush=True)
 
 
-def tile_sweep(torch, fa, w):
-    """Deviation study of the 16K causal workload: rows 0..2047 of heads 0..3
-    (a self-contained causal problem), every (Br, Bc) in {16, 32, 64, 128}^2
-    on the tile-study kernels plus the tuned default, max|dO| and max|dLSE|
-    against the FP64 oracle."""
+TILES = [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128)]
+
+
+def deviation_study(torch, fa, key, N, H, orders=True):
+    """The deviation study on a causal prefix of workload `key` (rows
+    0..N-1 of heads 0..H-1, a self-contained causal problem): output and LSE
+    deviation from the FP64 oracle for
+      * the tiled kernels at every (Br, Bc) in {16, 32, 64, 128}^2, with bf16
+        inputs and O rounded to bf16 ("bf16"), bf16 inputs and O left in fp32
+        ("bf16_f32out"), the running output rounded to bf16 after every key
+        tile ("bf16_acc16"), and fp32 inputs and arithmetic ("f32", the
+        unrounded float32 draw), plus the tuned default and fp16 I/O;
+      * key tiles visited last-first and shuffled (bf16_f32out);
+      * the materialised baseline with S and A held in fp32 or in bf16, O in
+        bf16 or fp32, and the fp32 baseline.
+    Each row: [precision, kernel, Br, Bc, max|dO|, mean|dO|, max|dLSE|]."""
     import numpy as np
     import oracle
-    from workloads import causal_prefix
-    inp = causal_prefix(w, N=2048, H=4)
-    o_ref, lse_ref = oracle.attention_f64(inp["q"], inp["k"], inp["v"], float(inp["scale"]), True)
+    from workloads import WORKLOADS, causal_prefix
+    w = WORKLOADS[key]
     dev = torch.device("cuda:0")
-    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    refs, dev_in = {}, {}
+    for fmt in ("bf16", "f32", "f16"):
+        inp = causal_prefix(w, N=N, H=H, fmt=fmt)
+        refs[fmt] = oracle.attention_f64(inp["q"], inp["k"], inp["v"], float(inp["scale"]), True)
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[fmt]
+        dev_in[fmt] = [torch.from_numpy(inp[n]).to(tdt).to(dev) for n in ("q", "k", "v")]
+    scale = float(np.float32(1.0 / math.sqrt(w.d)))
     rows = []
-    for br, bc in [(0, 0)] + [(a, b) for a in (16, 32, 64, 128) for b in (16, 32, 64, 128)]:
-        o, lse = fa.fwd(q, k, v, causal=True, scale=float(inp["scale"]), Br=br, Bc=bc)
+
+    def add(prec, kernel, br, bc, o, lse, ref_fmt):
         torch.cuda.synchronize()
+        o_ref, lse_ref = refs[ref_fmt]
         do = np.abs(o.double().cpu().numpy() - o_ref)
         dl = np.abs(lse.double().cpu().numpy() - lse_ref)
-        rows.append({"br": br or 128, "bc": bc or 64, "kernel": "tuned" if br == 0 else "tile-study",
-                     "max_dO": float(do.max()), "mean_dO": float(do.mean()), "max_dLSE": float(dl.max())})
-    return {"slice": "B1 H4 N2048 d128 causal (rows 0..2047 of heads 0..3)", "rows": rows}
+        rows.append([prec, kernel, br, bc, float("%.4g" % do.max()), float("%.4g" % do.mean()),
+                     float("%.4g" % dl.max())])
+
+    q, k, v = dev_in["bf16"]
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+    add("bf16", "tuned", 128, 64, o, lse, "bf16")
+    o32 = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    for br, bc in TILES:
+        o, lse = fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc)
+        add("bf16", "tiled", br, bc, o, lse, "bf16")
+        o, lse = fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, out=o32)
+        add("bf16_f32out", "tiled", br, bc, o, lse, "bf16")
+        o, lse = fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, acc16=True)
+        add("bf16_acc16", "tiled", br, bc, o, lse, "bf16")
+    if orders:
+        for name, order in (("tiled-desc", fa.ORDER_DESCENDING), ("tiled-shuffled", fa.ORDER_SHUFFLED)):
+            for br, bc in ((16, 16), (128, 64)):
+                o, lse = fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc, out=o32, tile_order=order)
+                add("bf16_f32out", name, br, bc, o, lse, "bf16")
+    for inter in ("f32", "io"):
+        o, lse = fa.baseline(q, k, v, causal=True, scale=scale, inter=inter)
+        add("bf16", "baseline-inter-" + ("f32" if inter == "f32" else "bf16"), 0, 0, o, lse, "bf16")
+        o, lse = fa.baseline(q, k, v, causal=True, scale=scale, inter=inter, out=o32)
+        add("bf16_f32out", "baseline-inter-" + ("f32" if inter == "f32" else "bf16"), 0, 0, o, lse, "bf16")
+    q, k, v = dev_in["f16"]
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+    add("f16", "tuned", 128, 64, o, lse, "f16")
+    o, lse = fa.baseline(q, k, v, causal=True, scale=scale, inter="f32")
+    add("f16", "baseline-inter-f32", 0, 0, o, lse, "f16")
+    q, k, v = dev_in["f32"]
+    for br, bc in TILES:
+        o, lse = fa.fwd(q, k, v, causal=True, scale=scale, Br=br, Bc=bc)
+        add("f32", "tiled", br, bc, o, lse, "f32")
+    o, lse = fa.baseline(q, k, v, causal=True, scale=scale, inter="f32")
+    add("f32", "baseline-inter-f32", 0, 0, o, lse, "f32")
+    return {"slice": f"{key}: rows 0..{N - 1} of heads 0..{H - 1} (causal prefix, B={w.B} d={w.d})",
+            "columns": ["precision", "kernel", "Br", "Bc", "max_dO", "mean_dO", "max_dLSE"], "rows": rows}
+
+
+def baseline_speed(torch, fa, w, inp, fa_ms, launches=3):
+    """Time of the materialised baseline (S and A in fp32, then in bf16) on
+    the full workload, next to the tiled kernel's: the speed-up of the
+    IO-aware method over the standard evaluation order."""
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    kl = torch.from_numpy(inp["key_len"]).to(dev) if inp["key_len"] is not None else None
+    bm = torch.from_numpy(inp["block_mask"]).to(dev) if inp["block_mask"] is not None else None
+    out = {}
+    for inter, code in (("f32", fa.DTYPE_F32), ("bf16", fa.DTYPE_BF16)):
+        need = fa.fa_fwd_baseline_workspace_size(w.B, w.H, w.N, fa.DTYPE_BF16, code)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def call():
+            fa.baseline(q, k, v, causal=w.causal, key_len=kl, block_mask=bm, scale=float(inp["scale"]),
+                        inter="f32" if inter == "f32" else "io", workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        out[f"inter_{inter}"] = {"ms": round(ms, 3), "workspace_gb": round(need / 1e9, 2),
+                                 "tiled_speedup": round(ms / fa_ms, 2)}
+        del ws
+    return out
 
 
 def n_curve(torch, fa, launches=20):

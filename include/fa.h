@@ -82,8 +82,26 @@ typedef enum {
  * half inputs and output, fp16 probabilities as the PV operand, fp32
  * arithmetic otherwise) is the other 16-bit format the page on
  * FlashAttention-2 adoption (tcdigital.jp, section on fp16/bf16 precision
- * support) names as the precisions the method is meant to run in. */
-enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F32 = 1, FA_DTYPE_F16 = 2 };
+ * support) names as the precisions the method is meant to run in.
+ * FA_DTYPE_BF16_F32OUT is the bf16 path with o a float [B, H, N, d] array
+ * that receives O before its final rounding (bf16 inputs, bf16
+ * probabilities as the PV operand): the deviation study of the page "Is
+ * Flash Attention Stable?" explainer (aibr.jp, sections 3 and 4) compares
+ * outputs with an FP64 golden value, and with O left unrounded the effect of
+ * the tiling is not hidden under the last rounding.  FA_DTYPE_BF16_ACC16 is
+ * bf16 I/O with the running output rounded to bf16 after every key tile, a
+ * model of an implementation that holds its partial output in the input
+ * precision between tiles, so that the output is rounded once per rescaling
+ * step (the section 3 explanation of why deviation falls as tiles grow);
+ * it is a study mode, less accurate than FA_DTYPE_BF16 by design.  Both run
+ * on the tile-study kernels (Br = Bc = 0 selects (128, 64)). */
+enum {
+    FA_DTYPE_BF16 = 0,
+    FA_DTYPE_F32 = 1,
+    FA_DTYPE_F16 = 2,
+    FA_DTYPE_BF16_F32OUT = 3,
+    FA_DTYPE_BF16_ACC16 = 4
+};
 
 /*
  * bf16 inputs and output (q, k, v, o point to bfloat16), fp32 arithmetic
@@ -114,15 +132,18 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
  * Attention Stable?" explainer (aibr.jp, sections 3 and 4: block sizes Br and
  * Bc varied, output compared with an FP64 golden value).  Same arguments as
  * fa_fwd plus:
- *   dtype : FA_DTYPE_BF16 (q/k/v/o bfloat16), FA_DTYPE_F16 (IEEE half) or
- *           FA_DTYPE_F32 (float)
+ *   dtype : FA_DTYPE_BF16 (q/k/v/o bfloat16), FA_DTYPE_F16 (IEEE half),
+ *           FA_DTYPE_F32 (float), FA_DTYPE_BF16_F32OUT (q/k/v bfloat16,
+ *           o float) or FA_DTYPE_BF16_ACC16 (bfloat16, running output
+ *           rounded to bf16 after every key tile)
  *   Br    : query rows per tile;  Bc : key rows per tile.
  * Br = Bc = 0 selects the tuned default (what fa_fwd / fa_fwd_f32 use).  For
  * bf16 every Br, Bc in {16, 32, 64, 128} is built for d = 64 and 128 (the
  * tile-study kernel family; an explicit (128, 64) runs it, not the tuned
  * kernel that the default (128, 64) runs), plus the tuned (256, 64), which
- * does not take a block mask.  fp16 builds (128, 64) for d = 64 and 128,
- * fp32 only its default.  Unbuilt pairs return FA_ERR_UNSUPPORTED_TILE.
+ * does not take a block mask.  FA_DTYPE_BF16_F32OUT, FA_DTYPE_BF16_ACC16 and
+ * fp32 build every Br, Bc in {16, 32, 64, 128} (fp32 default (128, 32));
+ * fp16 builds (128, 64).  Unbuilt pairs return FA_ERR_UNSUPPORTED_TILE.
  */
 int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int N, int d, float scale, int causal,
@@ -146,8 +167,9 @@ enum { FA_ORDER_ASCENDING = 0, FA_ORDER_DESCENDING = 1, FA_ORDER_SHUFFLED = 2 };
  *                Other values: FA_ERR_INVALID_ARG.
  * The result is the same attention up to rounding; only the order of the
  * running-maximum/rescale steps changes.  Orders other than ascending run
- * on the tile-study kernels only (bf16, d = 64 or 128, explicit Br, Bc in
- * {16, 32, 64, 128}); other tiles return FA_ERR_UNSUPPORTED_TILE.
+ * on the tile-study kernels only (bf16 with an explicit Br, Bc in
+ * {16, 32, 64, 128}, FA_DTYPE_BF16_F32OUT or FA_DTYPE_BF16_ACC16; d = 64 or
+ * 128); other tiles return FA_ERR_UNSUPPORTED_TILE.
  */
 int fa_fwd_study(const void *q, const void *k, const void *v, void *o, float *lse,
                  int B, int H, int N, int d, float scale, int causal,
@@ -234,6 +256,48 @@ int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *
                    int B, int H, int H_kv, int N, int d, float scale, int causal,
                    const int32_t *key_len, const uint8_t *block_mask,
                    hipStream_t stream, int dtype);
+
+/*
+ * Materialised ("baseline") attention: the same result as fa_fwd_ex computed
+ * in the conventional order, for the comparison that the page "Is Flash
+ * Attention Stable?" explainer (aibr.jp, opening dialogue and sections 3
+ * and 4) makes between FlashAttention and a Baseline Attention, each against
+ * an FP64 golden value at BF16.  Three kernels on `stream`:
+ *   S = scale * Q K^T, every (query, key) pair of every head, written to
+ *       `workspace` as [B, H, N, N] of the intermediate type (-inf where the
+ *       key is not allowed);
+ *   A = row-softmax(S) in place (fp32 arithmetic: max, sum of exp(S - max),
+ *       then exp(S - max) / sum), LSE = max + log(sum) (natural log);
+ *   O = A V (A rounded to the input type as the matrix-core operand, fp32
+ *       accumulation, O rounded once to the output type).
+ * Key tiles whose A entries are all exactly zero (past the causal diagonal
+ * or key_len, masked blocks) are skipped in A V.  Arguments as fa_fwd_ex
+ * (no tile choice) plus
+ *   dtype       : FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32 or
+ *                 FA_DTYPE_BF16_F32OUT
+ *   inter_dtype : type S and A are held in: FA_DTYPE_F32, or the input type
+ *                 of a 16-bit dtype (FA_DTYPE_BF16 for FA_DTYPE_BF16 and
+ *                 FA_DTYPE_BF16_F32OUT, FA_DTYPE_F16 for FA_DTYPE_F16:
+ *                 S and A each rounded once when written).  Other pairs:
+ *                 FA_ERR_UNSUPPORTED_TILE.
+ *   workspace   : DEVICE memory owned by the caller, 16-byte aligned, of at
+ *                 least fa_fwd_baseline_workspace_size(B, H, N, dtype,
+ *                 inter_dtype) bytes (else FA_ERR_INVALID_ARG; NULL:
+ *                 FA_ERR_NULL_PTR); overwritten (holds A afterwards).
+ * k and v have H heads (no grouping).  Outputs and the workspace must not
+ * overlap the inputs or each other (FA_ERR_INVALID_ARG).  Grids
+ * B*H*ceil(N/128)^2 and B*H*N must be below 2^31 (FA_ERR_INVALID_SHAPE).
+ */
+int fa_fwd_baseline(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const int32_t *key_len, const uint8_t *block_mask,
+                    hipStream_t stream, int dtype, int inter_dtype,
+                    void *workspace, size_t workspace_bytes);
+
+/* Workspace bytes fa_fwd_baseline needs: B * H * N * N elements of the
+ * intermediate type (0 for an unsupported (dtype, inter_dtype) pair or an
+ * invalid shape). */
+size_t fa_fwd_baseline_workspace_size(int B, int H, int N, int dtype, int inter_dtype);
 
 /*
  * Backward pass: the gradients of the loss sum(dout * o) with respect to q,

@@ -2,7 +2,8 @@
 
 The functions named after the C entry points (``fa_fwd``, ``fa_fwd_f32``,
 ``fa_fwd_ex``, ``fa_fwd_study``, ``fa_fwd_gqa``, ``fa_fwd_ws``, ``fa_fwd_workspace_size``,
-``fa_fwd_noalloc``, ``fa_bwd``, ``fa_bwd_ex``, ``fa_bwd_workspace_size``, ``fa_tile_shape``,
+``fa_fwd_noalloc``, ``fa_fwd_baseline``, ``fa_fwd_baseline_workspace_size``, ``fa_bwd``,
+``fa_bwd_ex``, ``fa_bwd_workspace_size``, ``fa_tile_shape``,
 ``fa_status_string``,
 ``fa_last_hip_error``) only marshal arguments to include/fa.h and raise
 ``FaError`` on a non-zero status; every step of the attention itself runs in
@@ -15,7 +16,8 @@ import math
 import os
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study", "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size",
-           "fa_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_bwd", "fa_bwd_ex",
+           "fa_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fa_fwd_baseline", "fa_fwd_baseline_workspace_size",
+           "baseline", "DTYPE_BF16_F32OUT", "DTYPE_BF16_ACC16", "fa_bwd", "fa_bwd_ex",
            "fa_bwd_workspace_size", "bwd",
            "fa_tile_shape", "ORDER_ASCENDING", "ORDER_DESCENDING", "ORDER_SHUFFLED",
            "fa_status_string", "fa_last_hip_error", "fwd", "library_path",
@@ -25,6 +27,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 DTYPE_F16 = 2
+DTYPE_BF16_F32OUT = 3
+DTYPE_BF16_ACC16 = 4
 ORDER_ASCENDING = 0
 ORDER_DESCENDING = 1
 ORDER_SHUFFLED = 2
@@ -86,6 +90,10 @@ def _load():
     lib.fa_fwd_ws.restype = i32
     lib.fa_fwd_noalloc.argtypes = [vp] * 5 + [i32] * 5 + [ctypes.c_float, i32, vp, vp, vp, i32]
     lib.fa_fwd_noalloc.restype = i32
+    lib.fa_fwd_baseline.argtypes = fwd_args + [i32, i32, vp, ctypes.c_size_t]
+    lib.fa_fwd_baseline.restype = i32
+    lib.fa_fwd_baseline_workspace_size.argtypes = [i32] * 5
+    lib.fa_fwd_baseline_workspace_size.restype = ctypes.c_size_t
     lib.fa_fwd_workspace_size.argtypes = [i32] * 5
     lib.fa_fwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -162,6 +170,17 @@ def fa_fwd_noalloc(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, key_len, bl
                                   block_mask, stream, dtype), "fa_fwd_noalloc")
 
 
+def fa_fwd_baseline(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream, dtype,
+                    inter_dtype, workspace, workspace_bytes):
+    _check(_load().fa_fwd_baseline(q, k, v, o, lse, B, H, N, d, scale, int(bool(causal)), key_len,
+                                   block_mask, stream, dtype, inter_dtype, workspace, workspace_bytes),
+           "fa_fwd_baseline")
+
+
+def fa_fwd_baseline_workspace_size(B, H, N, dtype, inter_dtype):
+    return int(_load().fa_fwd_baseline_workspace_size(B, H, N, dtype, inter_dtype))
+
+
 def fa_fwd_workspace_size(B, H, N, d, dtype):
     return int(_load().fa_fwd_workspace_size(B, H, N, d, dtype))
 
@@ -189,7 +208,8 @@ def fa_last_hip_error():
 
 
 def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, Bc=0,
-        out=None, lse=None, stream=None, tile_order=ORDER_ASCENDING, workspace=None):
+        out=None, lse=None, stream=None, tile_order=ORDER_ASCENDING, workspace=None,
+        acc16=False):
     """Attention forward on device tensors.
 
     q: contiguous [B, H, N, d] cuda tensor, bfloat16, float16 or float32; k, v: the
@@ -198,10 +218,14 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
     key_len: int32 cuda tensor [B] or None.  block_mask: uint8 cuda tensor with
     ceil(N/128)^2 entries (row = query block) or None.  scale defaults to
     1/sqrt(d).  Br/Bc = 0 selects the tuned tile.  Returns (o, lse) with o like
-    q and lse float32 [B, H, N]; `out`/`lse` may be passed preallocated, and
+    q and lse float32 [B, H, N]; `out`/`lse` may be passed preallocated (a
+    float32 `out` with bfloat16 inputs selects the fp32-output mode of the
+    tile-study kernels, O left unrounded), and
     lse=False skips the logsumexp (returned as None).  tile_order =
     ORDER_DESCENDING visits key tiles last-first, ORDER_SHUFFLED in a fixed
-    permutation (tile-study kernels only).  ``workspace`` (tuned tile only):
+    permutation (tile-study kernels only).  ``acc16`` (bfloat16 only, a
+    deviation-study mode): the running output is rounded to bf16 after every
+    key tile (FA_DTYPE_BF16_ACC16).  ``workspace`` (tuned tile only):
     True allocates the key-range split workspace ``fa_fwd_workspace_size``
     asks for (grids too small for the GPU), a uint8 cuda tensor is used as
     it, "static" uses the library's own static scratch (fa_fwd_noalloc,
@@ -211,7 +235,11 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k and v must share a dtype")
     if q.dtype == torch.bfloat16:
-        dtype = DTYPE_BF16
+        dtype = DTYPE_BF16_F32OUT if (out is not None and out.dtype == torch.float32) else DTYPE_BF16
+        if acc16:
+            if dtype != DTYPE_BF16:
+                raise ValueError("acc16 takes a bfloat16 output")
+            dtype = DTYPE_BF16_ACC16
     elif q.dtype == torch.float32:
         dtype = DTYPE_F32
     elif q.dtype == torch.float16:
@@ -277,6 +305,49 @@ def fwd(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, Br=0, 
                    lse.data_ptr() if want_lse else None, B, H, H_kv, N, d, float(scale),
                    causal, kl_ptr, bm_ptr, stream, dtype, Br, Bc)
     return out, (lse if want_lse else None)
+
+
+def baseline(q, k, v, causal=False, key_len=None, block_mask=None, scale=None, inter="f32",
+             out=None, lse=None, workspace=None, stream=None):
+    """Materialised attention (fa_fwd_baseline) on device tensors.
+
+    q, k, v: contiguous [B, H, N, d] cuda tensors of one dtype (bfloat16,
+    float16 or float32).  inter: "f32" holds S and A in float32, "io" in the
+    input type.  out: optional preallocated output (float32 with bfloat16
+    inputs keeps O unrounded).  workspace: optional uint8 cuda tensor of at
+    least fa_fwd_baseline_workspace_size bytes (allocated here if None).
+    Returns (o, lse).
+    """
+    import torch
+    codes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}
+    if q.dtype not in codes or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype among bfloat16, float16, float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.shape != q.shape:
+            raise ValueError(f"{name} must be a contiguous cuda tensor of q's shape")
+    B, H, N, d = q.shape
+    dtype = codes[q.dtype]
+    if out is None:
+        out = torch.empty_like(q)
+    if q.dtype == torch.bfloat16 and out.dtype == torch.float32:
+        dtype = DTYPE_BF16_F32OUT
+    if inter not in ("f32", "io"):
+        raise ValueError('inter must be "f32" or "io"')
+    inter_code = DTYPE_F32 if inter == "f32" else codes[q.dtype]
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = fa_fwd_baseline_workspace_size(B, H, N, dtype, inter_code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fa_fwd_baseline(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                    float(scale), causal, key_len.data_ptr() if key_len is not None else None,
+                    block_mask.data_ptr() if block_mask is not None else None, stream, dtype, inter_code,
+                    workspace.data_ptr(), workspace.numel())
+    return out, lse
 
 
 def bwd(q, k, v, o, dout, lse, causal=False, key_len=None, block_mask=None, scale=None,

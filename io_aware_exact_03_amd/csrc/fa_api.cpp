@@ -55,6 +55,15 @@ bool overlaps(const void *a, uint64_t a_bytes, const void *b, uint64_t b_bytes) 
     return x < y + b_bytes && y < x + a_bytes;
 }
 
+bool known_dtype(int dtype) {
+    return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_F16 ||
+           dtype == FA_DTYPE_BF16_F32OUT || dtype == FA_DTYPE_BF16_ACC16;
+}
+
+// Bytes per element of q/k/v and of o for a dtype code.
+uint64_t in_elem(int dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
+uint64_t out_elem(int dtype) { return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16_F32OUT ? 4 : 2; }
+
 const fa::Instance *find(const fa::Instance *table, int d, int causal, int br, int bc) {
     for (const fa::Instance *e = table; e->launch; ++e)
         if (e->d == d && e->causal == causal && e->br == br && e->bc == bc) return e;
@@ -69,11 +78,20 @@ const fa::Instance *find(const fa::Instance *table, int d, int causal, int br, i
 int resolve_tile(int dtype, int d, int block_sparse, int br, int bc, int causal,
                  const fa::Instance **out, int *br_out, int *bc_out, bool *study = nullptr) {
     if (study) *study = false;
-    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16)
-        return FA_ERR_UNSUPPORTED_TILE;
+    if (!known_dtype(dtype)) return FA_ERR_UNSUPPORTED_TILE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     const fa::Instance *inst = nullptr;
-    if (dtype == FA_DTYPE_F32) {
+    if (dtype == FA_DTYPE_BF16_F32OUT || dtype == FA_DTYPE_BF16_ACC16) {
+        // Output modes of the deviation study: the tile-study kernels only
+        // (default (128, 64)).
+        if (br == 0 && bc == 0) {
+            br = 128;
+            bc = 64;
+        }
+        inst = find(dtype == FA_DTYPE_BF16_F32OUT ? fa::bf16_f32out_instances() : fa::bf16_acc16_instances(), d,
+                    causal, br, bc);
+        if (inst && study) *study = true;
+    } else if (dtype == FA_DTYPE_F32) {
         if (br == 0 && bc == 0) fa::f32_default_tile(d, &br, &bc);
         inst = find(fa::f32_instances(), d, causal, br, bc);
     } else if (dtype == FA_DTYPE_F16) {
@@ -102,8 +120,7 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
     if (B < 1 || H < 1 || N < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16)
-        return FA_ERR_UNSUPPORTED_TILE;
+    if (!known_dtype(dtype)) return FA_ERR_UNSUPPORTED_TILE;
     // Grid size limit: B*H*ceil(N/16) workgroups at the smallest tile.
     const uint64_t groups = (uint64_t)B * (uint64_t)H * (((uint64_t)N + 15) / 16);
     if (groups >= (1ull << 31)) return FA_ERR_INVALID_SHAPE;
@@ -111,21 +128,21 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
         return FA_ERR_MISALIGNED;
     if ((lse && !aligned(lse, 4)) || (key_len && !aligned(key_len, 4))) return FA_ERR_MISALIGNED;
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-    const uint64_t elem = dtype == FA_DTYPE_F32 ? 4 : 2;
-    const uint64_t bytes = (uint64_t)B * H * N * d * elem;
-    const uint64_t kv_bytes = (uint64_t)B * Hkv * N * d * elem;
+    const uint64_t bytes = (uint64_t)B * H * N * d * in_elem(dtype);
+    const uint64_t o_bytes = (uint64_t)B * H * N * d * out_elem(dtype);
+    const uint64_t kv_bytes = (uint64_t)B * Hkv * N * d * in_elem(dtype);
     // Outputs (o, and lse when given) must not overlap any input or each
     // other: a workgroup writing them while others still read the inputs
     // would corrupt the result silently.
     const uint64_t lse_bytes = (uint64_t)B * H * N * sizeof(float);
     const struct { const void *p; uint64_t n; } ins[] = {{q, bytes}, {k, kv_bytes}, {v, kv_bytes}};
-    const struct { const void *p; uint64_t n; } outs[] = {{o, bytes}, {lse, lse ? lse_bytes : 0}};
+    const struct { const void *p; uint64_t n; } outs[] = {{o, o_bytes}, {lse, lse ? lse_bytes : 0}};
     for (const auto &w : outs) {
         if (!w.p) continue;
         for (const auto &r : ins)
             if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
     }
-    if (lse && overlaps(lse, lse_bytes, o, bytes)) return FA_ERR_INVALID_ARG;
+    if (lse && overlaps(lse, lse_bytes, o, o_bytes)) return FA_ERR_INVALID_ARG;
 
     if (order != FA_ORDER_ASCENDING && order != FA_ORDER_DESCENDING && order != FA_ORDER_SHUFFLED)
         return FA_ERR_INVALID_ARG;
@@ -141,7 +158,8 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     // static scratch (fa_fwd_noalloc) the workspace is the library's own
     // array, looked up only now that every argument has been checked.
     const uint64_t need = fa::fwd_workspace_bytes(B, H, N, d);
-    if (static_scratch && need > 0 && dtype != FA_DTYPE_F32) {
+    const bool splittable = dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
+    if (static_scratch && need > 0 && splittable) {
         if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_INVALID_SHAPE;
         hipError_t e = hipSuccess;
         const uintptr_t p = scratch_on_current_device(&e);
@@ -152,11 +170,11 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
         workspace = reinterpret_cast<void *>(p);
         workspace_bytes = FA_NOALLOC_SCRATCH_BYTES;
     }
-    const bool split = workspace && need > 0 && dtype != FA_DTYPE_F32;
+    const bool split = workspace && need > 0 && splittable;
     if (split) {
         if (workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
         if (overlaps(workspace, need, q, bytes) || overlaps(workspace, need, k, kv_bytes) ||
-            overlaps(workspace, need, v, kv_bytes) || overlaps(workspace, need, o, bytes) ||
+            overlaps(workspace, need, v, kv_bytes) || overlaps(workspace, need, o, o_bytes) ||
             (lse && overlaps(workspace, need, lse, lse_bytes)))
             return FA_ERR_INVALID_ARG;
     }
@@ -184,6 +202,56 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
 
     const hipError_t err = split ? fa::launch_fwd_split(a, d, causal ? 1 : 0, dtype == FA_DTYPE_F16 ? 1 : 0, stream)
                                  : inst->launch(a, stream);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
+// Element bytes of the baseline's intermediate type, or 0 when the
+// (dtype, inter_dtype) pair is not built: S and A in fp32, or in the input
+// type of a 16-bit dtype.
+uint64_t baseline_inter_bytes(int dtype, int inter) {
+    if (dtype == FA_DTYPE_BF16_ACC16 || !known_dtype(dtype)) return 0;
+    if (inter == FA_DTYPE_F32) return 4;
+    if (inter == FA_DTYPE_BF16 && (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_BF16_F32OUT)) return 2;
+    if (inter == FA_DTYPE_F16 && dtype == FA_DTYPE_F16) return 2;
+    return 0;
+}
+
+int baseline(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int N,
+             int d, float scale, int causal, const int32_t *key_len, const uint8_t *block_mask,
+             hipStream_t stream, int dtype, int inter, void *workspace, size_t workspace_bytes) {
+    if (!q || !k || !v || !o || !workspace) return FA_ERR_NULL_PTR;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    const uint64_t ib = baseline_inter_bytes(dtype, inter);
+    if (!ib) return FA_ERR_UNSUPPORTED_TILE;
+    // Grids: B*H*ceil(N/128)^2 score blocks and B*H*N softmax rows.
+    const uint64_t nt = ((uint64_t)N + 127) / 128, bhn = (uint64_t)B * H;
+    if (bhn * nt * nt >= (1ull << 31) || bhn * N >= (1ull << 31)) return FA_ERR_INVALID_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 16))
+        return FA_ERR_MISALIGNED;
+    if ((lse && !aligned(lse, 4)) || (key_len && !aligned(key_len, 4))) return FA_ERR_MISALIGNED;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const uint64_t need = bhn * N * (uint64_t)N * ib;
+    if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+    const uint64_t bytes = bhn * N * d * in_elem(dtype), o_bytes = bhn * N * d * out_elem(dtype);
+    const uint64_t lse_bytes = bhn * N * sizeof(float);
+    const struct { const void *p; uint64_t n; } ins[] = {{q, bytes}, {k, bytes}, {v, bytes}};
+    const struct { const void *p; uint64_t n; } outs[] = {{o, o_bytes}, {lse, lse ? lse_bytes : 0},
+                                                          {workspace, need}};
+    for (const auto &w : outs) {
+        if (!w.p) continue;
+        for (const auto &r : ins)
+            if (overlaps(w.p, w.n, r.p, r.n)) return FA_ERR_INVALID_ARG;
+        for (const auto &w2 : outs)
+            if (&w2 != &w && w2.p && overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_INVALID_ARG;
+    }
+    const hipError_t err = fa::launch_baseline(q, k, v, o, lse, key_len, block_mask, workspace, B, H, N, d,
+                                               scale, causal ? 1 : 0, dtype, inter == FA_DTYPE_F32 ? 1 : 0,
+                                               stream);
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
         return FA_ERR_HIP;
@@ -339,6 +407,20 @@ int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o, const 
               size_t workspace_bytes) {
     return backward(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
                     key_len, block_mask, stream, dtype, workspace, workspace_bytes);
+}
+
+int fa_fwd_baseline(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                    int N, int d, float scale, int causal, const int32_t *key_len,
+                    const uint8_t *block_mask, hipStream_t stream, int dtype, int inter_dtype,
+                    void *workspace, size_t workspace_bytes) {
+    return baseline(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, stream, dtype,
+                    inter_dtype, workspace, workspace_bytes);
+}
+
+size_t fa_fwd_baseline_workspace_size(int B, int H, int N, int dtype, int inter_dtype) {
+    const uint64_t ib = baseline_inter_bytes(dtype, inter_dtype);
+    if (!ib || B < 1 || H < 1 || N < 1) return 0;
+    return (size_t)((uint64_t)B * H * N * (uint64_t)N * ib);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int H_kv, int N, int d) {

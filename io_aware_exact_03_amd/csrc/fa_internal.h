@@ -41,6 +41,14 @@ uint64_t fwd_workspace_bytes(int B, int H, int N, int d);
 // for bf16 (f16 = 0) or fp16 (f16 = 1).
 hipError_t launch_fwd_split(const FwdArgs &a, int d, int causal, int f16, hipStream_t stream);
 
+// Enqueues the materialised baseline attention (scores to the workspace,
+// row softmax in place, then A V) for dtype 0 bf16, 1 fp32, 2 fp16 or 3 bf16
+// in / fp32 out; inter_f32 = 1 holds S and A in fp32, 0 in the input type.
+hipError_t launch_baseline(const void *q, const void *k, const void *v, void *o, float *lse,
+                           const int32_t *key_len, const uint8_t *block_mask, void *ws, int B, int H,
+                           int N, int d, float scale, int causal, int dtype, int inter_f32,
+                           hipStream_t stream);
+
 // Everything the backward kernels need.
 struct BwdArgs {
     const void *q, *k, *v, *o, *dout;  // bf16 or fp16 [B,H,N,d] (k, v: [B,Hkv,N,d])
@@ -96,6 +104,8 @@ struct Instance {
 const Instance *bf16_tuned_instances();
 const Instance *f16_tuned_instances();
 const Instance *bf16_instances();
+const Instance *bf16_f32out_instances();
+const Instance *bf16_acc16_instances();
 const Instance *f32_instances();
 void bf16_default_tile(int d, int block_sparse, int *br, int *bc);
 void f32_default_tile(int d, int *br, int *bc);

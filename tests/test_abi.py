@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_study",
                                            "fa_fwd_gqa", "fa_fwd_ws", "fa_fwd_workspace_size",
-                                           "fa_fwd_noalloc", "fa_bwd", "fa_bwd_ex",
+                                           "fa_fwd_noalloc", "fa_fwd_baseline",
+                                           "fa_fwd_baseline_workspace_size", "fa_bwd", "fa_bwd_ex",
                                            "fa_bwd_workspace_size", "fa_tile_shape",
                                            "fa_status_string", "fa_last_hip_error"])
 
@@ -60,9 +61,13 @@ def call(**kw):
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(B=1 << 20, H=1 << 10, N=1 << 10), 2),
     (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
     (dict(q=Q + 8), 4), (dict(o=O + 2), 4), (dict(lse=LSE + 2), 4), (dict(key_len=0x60000002), 4),
-    (dict(Br=48, Bc=64), 5), (dict(Br=128, Bc=256), 5), (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(Br=48, Bc=64), 5), (dict(Br=128, Bc=256), 5), (dict(dtype=5), 5), (dict(dtype=-1), 5),
     (dict(dtype=2, Br=64, Bc=32), 5),
-    (dict(dtype=1, Br=16, Bc=16), 5), (dict(d=64, Br=16, Bc=256), 5),
+    (dict(dtype=1, Br=256, Bc=64), 5), (dict(dtype=3, Br=256, Bc=64), 5), (dict(dtype=4, Br=256, Bc=64), 5),
+    (dict(dtype=6), 5),
+    (dict(d=64, Br=16, Bc=256), 5),
+    # fp32 output of the bf16-input mode: o is 4 bytes per element
+    (dict(dtype=3, o=Q - 2 * 3 * 100 * 64 * 2 - 16), 7),
     (dict(Br=256, Bc=64, block_mask=0x70000000), 5),
     (dict(scale=math.inf), 7), (dict(scale=math.nan), 7),
     (dict(o=Q + 64), 7), (dict(lse=O + 16), 7), (dict(lse=O - 2 * 3 * 100 * 4 + 4), 7),
@@ -302,3 +307,33 @@ def test_noalloc_invalid_arguments_return_status_without_launch(kw, status):
     names = ("q", "k", "v", "o", "lse", "B", "H", "H_kv", "N", "d", "scale", "causal", "key_len",
              "block_mask", "stream", "dtype")
     assert fa._load().fa_fwd_noalloc(*[args[n] for n in names]) == status
+
+
+WS = 0x7A000000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(workspace=None), 1), (dict(B=0), 2), (dict(N=0), 2), (dict(d=80), 3),
+    (dict(dtype=5), 5), (dict(dtype=4), 5), (dict(dtype=1, inter=0), 5), (dict(dtype=0, inter=2), 5),
+    (dict(dtype=2, inter=0), 5),
+    (dict(q=Q + 8), 4), (dict(workspace=WS + 4), 4), (dict(lse=LSE + 2), 4),
+    (dict(scale=math.inf), 7), (dict(ws_bytes=2 * 3 * 100 * 100 * 4 - 1), 7),
+    (dict(ws_bytes=2 * 3 * 100 * 100 * 2, inter=1), 7),
+    (dict(o=Q + 64), 7), (dict(lse=V + 16), 7), (dict(workspace=O + 16), 7), (dict(lse=WS + 64), 7),
+    (dict(B=1 << 12, H=1 << 12, N=1 << 10), 2),
+])
+def test_baseline_invalid_arguments_return_status_without_launch(kw, status):
+    args = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, N=100, d=64, scale=0.125, causal=0, key_len=None,
+                block_mask=None, stream=None, dtype=0, inter=1, workspace=WS, ws_bytes=1 << 30)
+    args.update(kw)
+    names = ("q", "k", "v", "o", "lse", "B", "H", "N", "d", "scale", "causal", "key_len", "block_mask",
+             "stream", "dtype", "inter", "workspace", "ws_bytes")
+    assert fa._load().fa_fwd_baseline(*[args[n] for n in names]) == status
+
+
+def test_baseline_workspace_size():
+    assert fa.fa_fwd_baseline_workspace_size(2, 3, 100, fa.DTYPE_BF16, fa.DTYPE_F32) == 2 * 3 * 100 * 100 * 4
+    assert fa.fa_fwd_baseline_workspace_size(2, 3, 100, fa.DTYPE_BF16, fa.DTYPE_BF16) == 2 * 3 * 100 * 100 * 2
+    assert fa.fa_fwd_baseline_workspace_size(1, 16, 16384, fa.DTYPE_BF16_F32OUT, fa.DTYPE_F32) == 16 * 16384 ** 2 * 4
+    assert fa.fa_fwd_baseline_workspace_size(1, 1, 10, fa.DTYPE_F32, fa.DTYPE_BF16) == 0
+    assert fa.fa_fwd_baseline_workspace_size(0, 1, 10, fa.DTYPE_F32, fa.DTYPE_F32) == 0

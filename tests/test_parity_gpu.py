@@ -347,6 +347,83 @@ def test_tile_study_d64(Br, Bc, mode):
     check(o, lse, *ref(inp), TOL_BF16, f"d=64 Br={Br} Bc={Bc} {mode}")
 
 
+def run_f32out(inp, Br=0, Bc=0, order=None):
+    """bf16 inputs, fp32 output (O before its final rounding): the
+    tile-study kernels in FA_DTYPE_BF16_F32OUT mode."""
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    kl = torch.from_numpy(inp["key_len"]).cuda() if inp.get("key_len") is not None else None
+    bm = torch.from_numpy(inp["block_mask"]).cuda() if inp.get("block_mask") is not None else None
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd(q, k, v, causal=inp["causal"], key_len=kl, block_mask=bm, scale=float(inp["scale"]), Br=Br, Bc=Bc,
+           out=out, lse=lse, tile_order=fa.ORDER_ASCENDING if order is None else order)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Br", [16, 32, 64, 128])
+@pytest.mark.parametrize("Bc", [16, 32, 64, 128])
+def test_bf16_f32out_tiles(d, Br, Bc):
+    """fp32-output mode of the tile-study kernels: within the bf16 bar of the
+    oracle, and exactly the bf16-output kernel's result once rounded to bf16
+    (round to nearest even), on every (Br, Bc) and two mask mixes."""
+    for mode in ("causal", "all"):
+        inp = custom(2, 2, 300, d, seed=400 + Br + Bc + d, **modes_for(300, 401)[mode])
+        o32, lse32 = run_f32out(inp, Br, Bc)
+        check(o32.double().cpu().numpy(), lse32.double().cpu().numpy(), *ref(inp), TOL_BF16,
+              f"f32out d={d} Br={Br} Bc={Bc} {mode}")
+        o16, lse16 = run(inp, Br=Br, Bc=Bc)
+        rounded = o32.to(torch.bfloat16).double().cpu().numpy()
+        assert np.array_equal(rounded, o16), f"f32out rounded != bf16 output, d={d} Br={Br} Bc={Bc} {mode}"
+        assert np.array_equal(lse32.double().cpu().numpy(), lse16)
+
+
+def test_bf16_f32out_default_tile_and_orders():
+    inp = long_causal_prefix()
+    if "ref" not in _PREFIX:
+        _PREFIX["ref"] = ref(inp)
+    for order in (fa.ORDER_ASCENDING, fa.ORDER_DESCENDING, fa.ORDER_SHUFFLED):
+        o, lse = run_f32out(inp, 0 if order == fa.ORDER_ASCENDING else 64, 0 if order == fa.ORDER_ASCENDING else 32,
+                            order)
+        check(o.double().cpu().numpy(), lse.double().cpu().numpy(), *_PREFIX["ref"], TOL_BF16, f"f32out order {order}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Br", [16, 32, 64, 128])
+@pytest.mark.parametrize("Bc", [16, 32, 64, 128])
+def test_bf16_acc16_tiles(d, Br, Bc):
+    """The study mode that rounds the running output to bf16 after every key
+    tile.  Each rounding moves the normalised output by at most u*max|v|
+    (u = 2^-8: the partial output never exceeds its row sum times max|v|,
+    and later rescaling and the final division only shrink that error), so
+    with T key tiles visited the bar is the bf16 bar plus T*u*max|v|; LSE
+    is untouched (the row sum stays fp32)."""
+    for mode in ("causal", "all"):
+        inp = custom(2, 2, 300, d, seed=600 + Br + Bc + d, **modes_for(300, 601)[mode])
+        q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+        kl = torch.from_numpy(inp["key_len"]).cuda() if inp.get("key_len") is not None else None
+        bm = torch.from_numpy(inp["block_mask"]).cuda() if inp.get("block_mask") is not None else None
+        o, lse = fa.fwd(q, k, v, causal=inp["causal"], key_len=kl, block_mask=bm, scale=float(inp["scale"]),
+                        Br=Br, Bc=Bc, acc16=True)
+        torch.cuda.synchronize()
+        tiles = -(-300 // Bc)
+        bar = TOL_BF16 + tiles * 2.0 ** -8 * float(np.abs(inp["v"]).max())
+        check(o.double().cpu().numpy(), lse.double().cpu().numpy(), *ref(inp), bar, f"acc16 d={d} Br={Br} Bc={Bc} {mode}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Br", [16, 32, 64, 128])
+@pytest.mark.parametrize("Bc", [16, 32, 64, 128])
+def test_f32_tiles(d, Br, Bc):
+    """The fp32 kernels at every (Br, Bc): within 1e-5 of the oracle on a
+    ragged length under every mask mix."""
+    for mode in ("dense", "causal", "padded", "blocks", "all"):
+        inp = custom(2, 2, 300, d, seed=500 + Br + Bc + d, dtype="f32", **modes_for(300, 501)[mode])
+        o, lse = run(inp, "f32", Br=Br, Bc=Bc)
+        check(o, lse, *ref(inp), TOL_F32, f"f32 d={d} Br={Br} Bc={Bc} {mode}")
+
+
 # ---------------------------------------------------------------- closed forms on the GPU
 
 
