@@ -52,8 +52,8 @@ PEAK_BF16_TFLOPS = 2516.6
 BF16_FLOP_PER_CLK = 256 * 4096
 PEAK_F32_MFMA_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fa_common.h", "fa_internal.h", "fa_bf16_tiles.h", "fa_fwd_bf16.hip",
-                  "fa_fwd_bf16_pipe.hip", "fa_fwd_f32.hip"]
+KERNEL_SOURCES = ["fa_common.h", "fa_internal.h", "fa_bf16_tiles.h", "fa_fwd_bf16_pipe.hip",
+                  "fa_fwd_flat.hip", "fa_fwd_f32.hip", "fa_study_kernel.h", "fa_fwd_bf16.hip"]
 
 
 def kernel_source_hash():

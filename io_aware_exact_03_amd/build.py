@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_bf16_pipe.hip", "fa_fwd_f32.hip", "fa_bwd.hip",
-           "fa_baseline.hip", "fa_fwd_study_modes.hip"]
+           "fa_baseline.hip", "fa_fwd_study_modes.hip", "fa_fwd_flat.hip"]
 ARCH = "gfx950"
 
 

@@ -610,11 +610,19 @@ hipError_t launch_split_typed(const FwdArgs &a, int d, int causal, hipStream_t s
     Instance{D, 0, 32 * NW, BC, &launch_pipe<T, D, BC, NS, NW, false>}, \
     Instance{D, 1, 32 * NW, BC, &launch_pipe<T, D, BC, NS, NW, true>}
 
+// The tuned (128, 64) tile at d = 64 runs fwd_flat (fa_fwd_flat.hip), four
+// workgroups per CU; the key-range split keeps fwd_pipe.
+hipError_t flat_bf16(const FwdArgs &a, hipStream_t s) { return launch_fwd_flat(a, 0, 0, s); }
+hipError_t flat_bf16_causal(const FwdArgs &a, hipStream_t s) { return launch_fwd_flat(a, 1, 0, s); }
+hipError_t flat_f16(const FwdArgs &a, hipStream_t s) { return launch_fwd_flat(a, 0, 1, s); }
+hipError_t flat_f16_causal(const FwdArgs &a, hipStream_t s) { return launch_fwd_flat(a, 1, 1, s); }
+
 }  // namespace
 
 const Instance *bf16_tuned_instances() {
     static const Instance table[] = {
-        FA_PIPE(__bf16, 64, 64, 2, 4),
+        Instance{64, 0, 128, 64, &flat_bf16},
+        Instance{64, 1, 128, 64, &flat_bf16_causal},
         FA_PIPE(__bf16, 64, 64, 2, 8),
         FA_PIPE(__bf16, 128, 64, 2, 4),
         FA_PIPE(__bf16, 128, 64, 2, 8),
@@ -625,7 +633,8 @@ const Instance *bf16_tuned_instances() {
 
 const Instance *f16_tuned_instances() {
     static const Instance table[] = {
-        FA_PIPE(_Float16, 64, 64, 2, 4),
+        Instance{64, 0, 128, 64, &flat_f16},
+        Instance{64, 1, 128, 64, &flat_f16_causal},
         FA_PIPE(_Float16, 128, 64, 2, 4),
         Instance{0, 0, 0, 0, nullptr},
     };

@@ -41,6 +41,11 @@ uint64_t fwd_workspace_bytes(int B, int H, int N, int d);
 // for bf16 (f16 = 0) or fp16 (f16 = 1).
 hipError_t launch_fwd_split(const FwdArgs &a, int d, int causal, int f16, hipStream_t stream);
 
+// Enqueues the d = 64 forward at four workgroups per CU (fwd_flat) for
+// bf16 (f16 = 0) or fp16 (f16 = 1); same arguments and results as the tuned
+// kernel.
+hipError_t launch_fwd_flat(const FwdArgs &a, int causal, int f16, hipStream_t stream);
+
 // Enqueues the materialised baseline attention (scores to the workspace,
 // row softmax in place, then A V) for dtype 0 bf16, 1 fp32, 2 fp16 or 3 bf16
 // in / fp32 out; inter_f32 = 1 holds S and A in fp32, 0 in the input type.
