@@ -151,10 +151,35 @@ def power_loop(torch, step, seconds=2.0, period=0.02):
         limit = amdsmi.amdsmi_get_power_info(h).get("power_limit")
     except Exception:
         limit = None
+
+    # Residency accumulators of the firmware's limiters (package power,
+    # thermal, PROCHOT) and, per XCD, the time the shader clock sat below
+    # the host's limit and why: their increase over the loop says which
+    # limiter held the clock down.
+    acc_keys = ("accumulation_counter", "ppt_residency_acc", "socket_thm_residency_acc", "vr_thm_residency_acc",
+                "hbm_thm_residency_acc", "prochot_residency_acc", "xcp_stats.gfx_busy_acc",
+                "xcp_stats.gfx_below_host_limit_acc", "xcp_stats.gfx_below_host_limit_ppt_acc",
+                "xcp_stats.gfx_below_host_limit_thm_acc", "xcp_stats.gfx_below_host_limit_total_acc",
+                "xcp_stats.gfx_low_utilization_acc")
+
+    def flat_numbers(x):
+        if isinstance(x, (int, float)):
+            return [x]
+        if isinstance(x, (list, tuple)):
+            return [y for z in x for y in flat_numbers(z)]
+        return []
+
+    def accumulators():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        except Exception:
+            return {}
+        return {k: sum(flat_numbers(m.get(k))) for k in acc_keys if flat_numbers(m.get(k))}
     torch.cuda.synchronize()
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
     time.sleep(3 * period)
+    a0 = accumulators()
     e0 = energy()
     t0 = time.perf_counter()
     n = 0
@@ -167,6 +192,7 @@ def power_loop(torch, step, seconds=2.0, period=0.02):
             break
     t1 = time.perf_counter()
     e1 = energy()
+    a1 = accumulators()
     stop.set()
     th.join()
     busy = [x for x in samples if t0 + 0.1 <= x["t"] <= t1]
@@ -185,6 +211,7 @@ def power_loop(torch, step, seconds=2.0, period=0.02):
         "avg_power_from_energy_w": round(joules / (t1 - t0), 1),
         "throttle_status_seen": sorted({x["throttle"] for x in busy if x["throttle"] not in (None, "N/A")}),
         "hotspot_c_max": max(num("hotspot")) if num("hotspot") else None,
+        "limiter_accumulator_deltas": {k.replace("xcp_stats.", "xcd_sum."): a1[k] - a0[k] for k in a1 if k in a0},
     }
     try:
         amdsmi.amdsmi_shut_down()

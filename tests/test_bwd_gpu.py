@@ -168,7 +168,7 @@ def test_bwd_split_deterministic():
 def test_bwd_full_size_sampled(workload):
     # The whole workload at its full size, in the launch configuration the
     # backward report times; dQ checked on sampled query rows, dK and dV on
-    # sampled keys of one key/value head, each against the FP64 oracle
+    # sampled keys of two key/value heads, each against the FP64 oracle
     # evaluated for just those outputs.
     w = WORKLOADS[workload]
     inp = make_inputs(w)
@@ -182,10 +182,15 @@ def test_bwd_full_size_sampled(workload):
     dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, key_len=kl, block_mask=bm, scale=scale)
     torch.cuda.synchronize()
     B, H, N, d = inp["q"].shape
-    rows = rng.choice(B * H * N, size=24, replace=False)
-    x = int(rng.integers(B * H))  # one key/value head (H_kv = H here)
-    keys = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=10, replace=False)]))
-    cols = x * N + keys
+    # 256 query rows over all heads (plus the first and last rows of the
+    # grid); 40 keys (plus keys 0 and N-1) in each of two key/value heads
+    # (H_kv = H here), the first and last head of the grid among them
+    rows = np.unique(np.concatenate([[0, N - 1, B * H * N - 1], rng.choice(B * H * N, size=256, replace=False)]))
+    cols = []
+    for x in (0, B * H - 1) if B * H > 1 else (0,):
+        keys = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=40, replace=False)]))
+        cols.append(x * N + keys)
+    cols = np.concatenate(cols)
     args = (scale, w.causal, inp["key_len"], inp["block_mask"])
     dout = tdo.float().cpu().numpy()
     ref_dq = oracle.attention_bwd_rows_f64(inp["q"], inp["k"], inp["v"], dout, rows, *args)
