@@ -133,10 +133,10 @@ def power_loop(torch, step, seconds=2.0, period=0.02):
         while not stop.is_set():
             try:
                 m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+                clks = sorted(c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0)
                 samples.append(dict(t=time.perf_counter(), power=m.get("current_socket_power"),
-                                    clk=sum(clks) / len(clks) if clks else m.get("current_gfxclk"),
-                                    clk_min=min(clks) if clks else None,
+                                    clk=clks[len(clks) // 2] if clks else m.get("current_gfxclk"),
+                                    clk_min=clks[0] if clks else None,
                                     throttle=m.get("throttle_status"),
                                     hotspot=m.get("temperature_hotspot")))
             except Exception:
@@ -205,7 +205,9 @@ def power_loop(torch, step, seconds=2.0, period=0.02):
         "board_power_w_avg": round(mean(pw), 1) if pw else None,
         "board_power_w_max": max(pw) if pw else None,
         "power_limit_w": limit,
-        "gfx_clock_ghz": round(mean(clk) / 1000.0, 4) if clk else None,
+        # median over samples of each sample's median XCD clock (single
+        # readings of an XCD between dispatches can be far below the rest)
+        "gfx_clock_ghz": round(sorted(clk)[len(clk) // 2] / 1000.0, 4) if clk else None,
         "gfx_clock_ghz_min_xcd": round(min(cmin) / 1000.0, 4) if cmin else None,
         "energy_j_per_launch": round(joules / n, 6) if n else None,
         "avg_power_from_energy_w": round(joules / (t1 - t0), 1),
