@@ -203,7 +203,8 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
  *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
  * the same combination that merges results computed on different key
  * ranges anywhere.  Same arguments as fa_fwd_gqa with the tuned tile, plus
- *   dtype     : FA_DTYPE_BF16 or FA_DTYPE_F16 (FA_DTYPE_F32 runs unsplit)
+ *   dtype     : FA_DTYPE_BF16 or FA_DTYPE_F16 (the other dtypes run
+ *               unsplit, as fa_fwd_gqa with Br = Bc = 0)
  *   workspace : DEVICE memory owned by the caller (16-byte aligned) of
  *               workspace_bytes bytes, or NULL.  fa_fwd_workspace_size
  *               gives the bytes needed; when it is 0, or workspace is NULL,
