@@ -149,6 +149,10 @@ def power_loop(torch, step, seconds=2.0, period=0.02):
 
     try:
         limit = amdsmi.amdsmi_get_power_info(h).get("power_limit")
+        # Some amdsmi releases report this field in microwatts, others in
+        # watts; no board draws 100 kW, so a larger figure is microwatts.
+        if isinstance(limit, (int, float)) and limit > 1e5:
+            limit = limit / 1e6
     except Exception:
         limit = None
 

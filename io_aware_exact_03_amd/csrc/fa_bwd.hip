@@ -16,16 +16,20 @@
 // Kernels:
 //  * bwd_delta: Delta_i = dO_i . O_i per query row (fp32, caller workspace).
 //  * bwd_dkdv: one workgroup per block of 32*NW keys of one key/value head;
-//    each wave keeps its 32 keys' K and V fragments and the dK^T, dV^T
-//    accumulators in registers and walks the query tiles (32*QT rows of Q
-//    and dO, with their LSE and Delta, staged in LDS per step) of every
-//    query head that reads this key/value head.  Per step: S = Q K^T and dP = dO V^T (lane = key),
-//    then dV^T += dO^T P^T and dK^T += Q^T dS^T.  Used for d = 64 without
-//    the causal mask.
-//  * bwd_dkdv_pair (d = 128, and causal d = 64): the same product chain with
-//    8 waves per 128 keys, two waves per 32 keys splitting each 64-row query
-//    tile, so that a wave's registers fit two waves per SIMD at d = 128; the
-//    pair's partial dK, dV are added through LDS at the end.
+//    each wave keeps its 32 keys' K fragments (and, unless VL, V fragments)
+//    and the dK^T, dV^T accumulators in registers and walks the query tiles
+//    (32*QT rows of Q and dO, with their LSE and Delta, staged in LDS per
+//    step) of every query head that reads this key/value head.  Per step:
+//    S = Q K^T and dP = dO V^T (lane = key), then dV^T += dO^T P^T and
+//    dK^T += Q^T dS^T.  Used for d = 64 without the causal mask (V in
+//    registers, 64 rows per step) and for d = 128 grids of two or more
+//    rounds (VL: V read from the key block's LDS tile, 32 rows per step;
+//    two workgroups per CU).
+//  * bwd_dkdv_pair (causal d = 64, and d = 128 grids that fill the CUs
+//    only once): the same product chain with 8 waves per 128 keys, two
+//    waves per 32 keys splitting each 64-row query tile, so that a wave's
+//    registers fit two waves per SIMD at d = 128; the pair's partial dK, dV
+//    are added through LDS at the end.
 //  * bwd_dq: one workgroup per 32*NW query rows; each wave keeps its rows'
 //    Q and dO fragments and the dQ^T accumulator in registers and walks the
 //    key tiles (64 keys of K and V staged in LDS per step, taken as two
@@ -163,9 +167,10 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 // run in ascending order.  Causal grids, where key block kt is seen by the
 // query rows from kt on (the first blocks the most), use the CU-balanced
 // order of xcd_item_causal instead (heaviest blocks of every head first).
-__device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt, bool causal) {
-    // the causal dK/dV kernel (the pair kernel) fits one workgroup per CU
-    int id = causal ? xcd_item_causal(nkt * nsplit, 1) : xcd_item(nkt * nsplit);
+__device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt, bool causal,
+                                           int resident) {
+    // resident: workgroups of the kernel that fit one CU together
+    int id = causal ? xcd_item_causal(nkt * nsplit, resident) : xcd_item(nkt * nsplit);
     *split = id % nsplit;
     id /= nsplit;
     *bkv = id / nkt;
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a, int64_t el) {
     *reinterpret_cast<x4_t *>(reinterpret_cast<T *>(a.dv) + i) = wv;
 }
 
-template <class T, int D, int NW, int QT, bool CAUSAL>
+template <class T, int D, int NW, int QT, bool CAUSAL, bool VL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     using x8_t = typename Elem<T>::x8;
     using x4_t = typename Elem<T>::x4;
@@ -207,6 +212,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) T q_lds[2][BQ * D];
     __shared__ __attribute__((aligned(1024))) T do_lds[2][BQ * D];
     __shared__ __attribute__((aligned(16))) float ld_lds[2][2 * BQ];
+    // VL: the key block's V rows, loaded once (the V^T fragments are read
+    // from here at every step instead of being held in registers).
+    __shared__ __attribute__((aligned(1024))) T v_lds[VL ? BK * D : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     // Workgroup -> (batch, key/value head, key block, query-head split);
     // causal grids start with the key blocks that see the most query rows.
     int split, bkv, kt;
-    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL);
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL, 2);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + wave * 32;
@@ -231,16 +239,17 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     // This wave's 32 keys as B operands: K^T and V^T fragments (lane: key
     // lane % 32, head dims 16*ks + 8*(lane/32) .. +7).
     const int key = kw0 + lane % 32;
-    x8_t kf[NQK], vf[NQK];
+    x8_t kf[NQK], vf[VL ? 1 : NQK];
 #pragma unroll
     for (int ks = 0; ks < NQK; ++ks) {
         u32x4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
         if (key < N) {
             xk = *reinterpret_cast<const u32x4_t *>(K + (int64_t)key * D + ks * 16 + 8 * (lane / 32));
-            xv = *reinterpret_cast<const u32x4_t *>(V + (int64_t)key * D + ks * 16 + 8 * (lane / 32));
+            if constexpr (!VL)
+                xv = *reinterpret_cast<const u32x4_t *>(V + (int64_t)key * D + ks * 16 + 8 * (lane / 32));
         }
         kf[ks] = __builtin_bit_cast(x8_t, xk);
-        vf[ks] = __builtin_bit_cast(x8_t, xv);
+        if constexpr (!VL) vf[ks] = __builtin_bit_cast(x8_t, xv);
     }
     f32x16_t dk[ND], dv[ND];
 #pragma unroll
@@ -301,7 +310,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     };
 
     int s = next_step(s_lo);
-    if (s < nsteps) issue(s, 0);
+    if (s < nsteps) {
+        // (rows past N re-read row N-1; those keys get p = 0)
+        if constexpr (VL) copy_rows<D, NW, BK>(V, k0, N, v_lds, wave, lane);
+        issue(s, 0);
+    }
+    const T *vw = v_lds + wave * 32 * D;  // VL: this wave's 32 V rows
     int buf = 0;
     while (s < nsteps) {
         const int sn = next_step(s + 1);
@@ -324,8 +338,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
                 for (int ks = 0; ks < NQK; ++ks) {
                     const x8_t qa = *reinterpret_cast<const x8_t *>(Qs + (rbase ^ (ks << 4)));
                     const x8_t da = *reinterpret_cast<const x8_t *>(dOs + (rbase ^ (ks << 4)));
+                    x8_t vb;
+                    if constexpr (VL)
+                        vb = *reinterpret_cast<const x8_t *>(vw + (rbase ^ (ks << 4)));
+                    else
+                        vb = vf[ks];
                     sacc = mfma(qa, kf[ks], sacc);
-                    dpacc = mfma(da, vf[ks], dpacc);
+                    dpacc = mfma(da, vb, dpacc);
                 }
                 const bool edge = (qs + 32 > N) || (kw0 + 32 > kv_len) || (CAUSAL && qs < kw0 + 31);
                 // P and dS in place; this lane's 16 rows are 4 groups of 4
@@ -441,7 +460,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     const int N = a.N;
     const int nkt = (N + BK - 1) / BK;
     int split, bkv, kt;
-    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL);
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL, 1);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + kg * 32;
@@ -835,10 +854,23 @@ hipError_t launch_bwd_impl(const BwdArgs &a, hipStream_t stream) {
     // workgroups per CU (128 rows would spill)
     constexpr int QT = 2;
     const unsigned kgrid = (unsigned)(nkt * a.B * a.Hkv * a.nsplit);
-    if constexpr (D == 128 || CAUSAL)
+    // d = 128: two 4-wave workgroups per CU (32 query rows per step, V read
+    // from LDS) when the grid fills the CUs twice over; the two waves of a
+    // SIMD then belong to different workgroups and their phases (products,
+    // exponentials, transposed reads) overlap instead of meeting at one
+    // barrier.  A causal grid of one round or less would pair each heavy
+    // key block with a light one and leave the heavy one alone on its CU at
+    // one wave per SIMD: the 8-wave pair kernel is faster there.
+    if constexpr (D == 128) {
+        if (kgrid >= 1024u || (!CAUSAL && kgrid >= 512u))
+            hipLaunchKernelGGL((bwd_dkdv<T, D, NW, 1, CAUSAL, true>), dim3(kgrid), dim3(NW * 64), 0, stream, a);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_pair<T, D, CAUSAL>), dim3(kgrid), dim3(512), 0, stream, a);
+    } else if constexpr (CAUSAL) {
         hipLaunchKernelGGL((bwd_dkdv_pair<T, D, CAUSAL>), dim3(kgrid), dim3(512), 0, stream, a);
-    else
-        hipLaunchKernelGGL((bwd_dkdv<T, D, NW, QT, CAUSAL>), dim3(kgrid), dim3(NW * 64), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((bwd_dkdv<T, D, NW, QT, CAUSAL, false>), dim3(kgrid), dim3(NW * 64), 0, stream, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.nsplit > 1) {

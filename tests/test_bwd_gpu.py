@@ -99,6 +99,42 @@ def test_bwd_modes(d, N, mode):
     run_case(2, 2, 2, N, d, seed=70 + N + d, **modes(N, 71)[mode])
 
 
+def key_lengths(B, N, rng):
+    """Ragged key lengths for B batch entries: one with no key, one full."""
+    kl = rng.integers(0, N + 1, B)
+    kl[0], kl[-1] = 0, N
+    return kl
+
+
+@pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
+def test_bwd_two_per_cu_modes(mode):
+    """d = 128 grids of 1040 key blocks (B13 H16 N520: five 128-key blocks
+    per head, the last ragged) run the dK/dV kernel at two 4-wave
+    workgroups per CU (smaller grids take the pair kernel); every mask
+    mode, gradients start as NaN."""
+    B, H, N = 13, 16, 520
+    rng = np.random.default_rng(400)
+    kw = {"dense": {}, "causal": dict(causal=True), "padded": dict(key_len=key_lengths(B, N, rng)),
+          "blocks": dict(block_mask=band_global_block_mask(5, rng, n_global=1)),
+          "all": dict(causal=True, key_len=key_lengths(B, N, rng),
+                      block_mask=band_global_block_mask(5, rng, n_global=1))}[mode]
+    run_case(B, H, H, N, 128, seed=401, **kw)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (8, 2)])
+def test_bwd_two_per_cu_split(causal, H, H_kv):
+    """B4 N1000 d128 with the split workspace: 64 key blocks split 16 ways
+    over their (query head, query tile) steps, a 1024-workgroup grid of the
+    two-per-CU dK/dV kernel writing fp32 partials."""
+    assert fa.fa_bwd_workspace_size(4, H, H_kv, 1000, 128) > 0
+    run_case(4, H, H_kv, 1000, 128, seed=402, causal=causal, workspace=True)
+
+
+def test_bwd_two_per_cu_f16():
+    run_case(13, 16, 16, 520, 128, seed=403, causal=True, dtype="f16")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 45, 300, 1000])
 @pytest.mark.parametrize("mode", ["dense", "causal", "padded", "blocks", "all"])
