@@ -315,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
         if constexpr (VL) copy_rows<D, NW, BK>(V, k0, N, v_lds, wave, lane);
         issue(s, 0);
     }
-    const T *vw = v_lds + wave * 32 * D;  // VL: this wave's 32 V rows
+    const T *vw = VL ? v_lds + wave * 32 * D : v_lds;  // VL: this wave's 32 V rows
     int buf = 0;
     while (s < nsteps) {
         const int sn = next_step(s + 1);
