@@ -134,6 +134,20 @@ __device__ __forceinline__ f32x16_t mfma(f16x8_t a, f16x8_t b, f32x16_t c) {
 // Row of accumulator value i of lane l in a 32x32 product block.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
+// A staged tile's log-sum-exps in the form the exponentials take them:
+// -LSE * log2(e), and -inf for a row with no allowed key (its p is then 0).
+// Run by wave 0, which issued the LSE copy into LDS and has waited for it,
+// once per row of the tile instead of once per score; the next barrier
+// publishes it.
+__device__ __forceinline__ void lse_to_neg_log2(float *l, int rows) {
+    // the lane index recomputed here rather than kept live across the loop
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    if (lane < rows) {
+        const float x = l[lane];
+        l[lane] = x == kNegInf ? kNegInf : -(x * 1.44269504088896341f);
+    }
+}
+
 // ---------------------------------------------------------------- Delta
 
 template <class T, int D>
@@ -314,6 +328,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
         // (rows past N re-read row N-1; those keys get p = 0)
         if constexpr (VL) copy_rows<D, NW, BK>(V, k0, N, v_lds, wave, lane);
         issue(s, 0);
+        if (wave == 0) {
+            wait_copies();
+            lse_to_neg_log2(ld_lds[0], BQ);
+        }
     }
     const T *vw = VL ? v_lds + wave * 32 * D : v_lds;  // VL: this wave's 32 V rows
     int buf = 0;
@@ -357,9 +375,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int i = 4 * gi + j;
-                        // a row with no allowed key (LSE = -inf) gets p = 0
-                        const float l2 = l4[j] == kNegInf ? __builtin_inff() : l4[j] * 1.44269504088896341f;
-                        float p = fast_exp2(fmaf(sacc[i], c, -l2));
+                        // l4: -LSE * log2(e) of the row (lse_to_neg_log2)
+                        float p = fast_exp2(fmaf(sacc[i], c, l4[j]));
                         if (edge) {
                             const int qi = qs + acc_row(i, lane);
                             const bool ok = qi < N && key < kv_len && (!CAUSAL || key <= qi);
@@ -368,6 +385,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
                         dpacc[i] = p * (dpacc[i] - d4[j]);
                         sacc[i] = p;
                     }
+                    // VL at d = 128 sits at 256 registers: without this fence
+                    // the scheduler hoists later groups' reads and spills
+                    if constexpr (VL) __builtin_amdgcn_sched_barrier(0);
                 }
                 // dV^T += dO^T P^T and dK^T += Q^T dS^T over the two 16-row chunks.
 #pragma unroll
@@ -387,6 +407,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
                     }
                 }
             }
+        }
+        if (sn < nsteps && wave == 0) {
+            wait_copies();
+            lse_to_neg_log2(ld_lds[buf ^ 1], BQ);
         }
         s = sn;
         buf ^= 1;
@@ -529,6 +553,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     int s = next_step(s_lo);
     if (s < nsteps) issue(s, 0);
     wait_copies();
+    if (s < nsteps && wave == 0) lse_to_neg_log2(ld_lds[0], BQ);
     __syncthreads();
     // This wave's K^T fragments (B operand of S = Q K^T), kept in registers.
     x8_t kf[NQK];
@@ -566,8 +591,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int i = 4 * gi + j;
-                    const float l2 = l4[j] == kNegInf ? __builtin_inff() : l4[j] * 1.44269504088896341f;
-                    float p = fast_exp2(fmaf(sacc[i], c, -l2));
+                    float p = fast_exp2(fmaf(sacc[i], c, l4[j]));  // l4: -LSE * log2(e)
                     if (edge) {
                         const int qi = qs + acc_row(i, lane);
                         const bool ok = qi < N && key < kv_len && (!CAUSAL || key <= qi);
@@ -593,6 +617,10 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
                     dk[mb] = mfma(qtr, dsf, dk[mb]);
                 }
             }
+        }
+        if (sn < nsteps && wave == 0) {
+            wait_copies();
+            lse_to_neg_log2(ld_lds[buf ^ 1], BQ);
         }
         s = sn;
         buf ^= 1;
