@@ -35,6 +35,9 @@ Prints ONE JSON line:
               speed-up over it
   n_curve     TFLOP/s and fraction of the bf16 peak at N = 1K..16K (16 heads,
               B = 16384/N, d = 64 and 128, causal and not)
+  backward    (bf16 workloads) the backward pass (fa_bwd) on the same
+              workload and forward outputs with a seeded N(0,1) dO: median
+              launch time and TFLOP/s at 10*d FLOP per visible pair
 """
 import argparse
 import hashlib
@@ -455,6 +458,8 @@ def main():
         if w.dtype == "bf16":
             line["baseline_attention"] = baseline_speed(torch, fa, w, inp, kern_ms)
         line["n_curve"] = n_curve(torch, fa)
+        if w.dtype == "bf16":
+            line["backward"] = backward_speed(torch, fa, w, q, k, v, out, lse, kl, bm, scale, pairs)
     print(json.dumps(line), flush=True)
 
 
@@ -561,6 +566,37 @@ def baseline_speed(torch, fa, w, inp, fa_ms, launches=3):
                                  "tiled_speedup": round(ms / fa_ms, 2)}
         del ws
     return out
+
+
+def backward_speed(torch, fa, w, q, k, v, o, lse, kl, bm, scale, pairs, launches=10):
+    """Median launch time of fa_bwd on the workload (its forward's O and LSE,
+    dO drawn N(0,1) on the GPU from a seeded generator), and its rate at
+    10*d FLOP per visible pair (five products of 2*d)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 7)
+    dout = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def call():
+        fa.bwd(q, k, v, o, dout, lse, causal=w.causal, key_len=kl, block_mask=bm, scale=scale,
+               dq=dq, dk=dk, dv=dv, delta=delta)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    st = torch.cuda.current_stream()
+    for e0, e1 in ev:
+        e0.record(st)
+        call()
+        e1.record(st)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[launches // 2]
+    tf = 10 * w.d * pairs / (ms * 1e-3) / 1e12
+    del dout, dq, dk, dv, delta
+    return {"us": round(ms * 1e3, 1), "tflops_10d": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "launches": launches}
 
 
 def n_curve(torch, fa, launches=20):
