@@ -269,9 +269,10 @@ def test_bwd_deterministic():
 
 def test_gqa_full_size_sampled():
     # Grouped heads at the 16K causal shape (B1 H16 N16384 d128, four query
-    # heads per key/value head): forward O and LSE on sampled rows, dQ on
-    # sampled rows, dK and dV on sampled keys of one key/value head (summed
-    # over its four query heads by the oracle).
+    # heads per key/value head; its 512-workgroup dK/dV grid runs the 8-wave
+    # pair kernel): forward O and LSE on sampled rows, dQ on sampled rows,
+    # dK and dV on sampled keys of the last key/value head (summed over its
+    # four query heads by the oracle).
     B, H, Hkv, N, d = 1, 16, 4, 16384, 128
     rng = np.random.Generator(np.random.PCG64(3004))
     q = random_qkv(B, H, N, d, 0, "bf16", 0.5, rng=rng)[0]
@@ -282,8 +283,10 @@ def test_gqa_full_size_sampled():
     o, lse = fa.fwd(tq, tk, tv, causal=True, scale=scale)
     dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True, scale=scale)
     torch.cuda.synchronize()
-    rows = rng.choice(B * H * N, size=24, replace=False)
-    cols = int(rng.integers(B * Hkv)) * N + np.unique(np.concatenate([[0, N - 1], rng.choice(N, 6)]))
+    rows = np.unique(np.concatenate([[0, B * H * N - 1], rng.choice(B * H * N, size=128, replace=False)]))
+    # (one key/value head: the oracle runs the forward of its four query
+    # heads at full length for these keys)
+    cols = (B * Hkv - 1) * N + np.unique(np.concatenate([[0, N - 1], rng.choice(N, 40, replace=False)]))
     o_ref, l_ref = oracle.attention_rows_f64(q, k, v, rows, scale, True)
     dout = tdo.float().cpu().numpy()
     ref = {"dq": oracle.attention_bwd_rows_f64(q, k, v, dout, rows, scale, True)}
