@@ -107,8 +107,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     constexpr int NB = NKB * 2 * ND;       // PV products per tile
     constexpr int NS = NA + NB;            // matrix-core slots per step
     constexpr int NF = 2 * NKB;            // 8-score P fragments per tile
-    constexpr int LA = 3;                  // K fragment reads run LA slots ahead
-    constexpr int LB = 2;                  // V fragment reads run LB slots ahead
+    // K and V fragment reads run LA and LB slots ahead of their products.
+    // Swept on the 16K causal workload (same box, alternating runs): LB = 1
+    // +2-3 %; LA = 4, LB = 3 -0.5-1 % on the workload's data and -2 % on
+    // all-zero inputs against LA = 3, LB = 2; larger distances no better.
+    constexpr int LA = 4;
+    constexpr int LB = 3;
     using Plan = ChunkPlan<NF>;
     // PV product pv uses fragment pv / ND; its packing must come earlier.
     static_assert(Plan::packed_in_time(NA, ND, NS), "every P fragment packed before its PV product");
