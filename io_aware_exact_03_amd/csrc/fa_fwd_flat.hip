@@ -9,7 +9,7 @@
 //
 //  * fwd_pipe keeps two tiles' scores in registers (the next tile's S = K Q^T
 //    runs on the matrix cores while this tile's softmax runs on the VALU),
-//    which needs 154 VGPRs at d = 64: three workgroups per CU.
+//    which needs over 128 VGPRs at d = 64: three workgroups per CU.
 //  * fwd_flat computes one tile at a time (scores, softmax, P V) in at most
 //    128 VGPRs, so four workgroups (four waves per SIMD) are resident per CU
 //    and the overlap of matrix-core and VALU work comes from the other waves
