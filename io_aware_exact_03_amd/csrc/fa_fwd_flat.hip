@@ -120,10 +120,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_flat(FwdArgs a) {
             for (int i = 0; i < ROUNDS; ++i) lds_copy16(base, off[i], dst + (wave + NW * i) * 512);
         } else {
             // Last, partial tile: rows past the last valid key re-read it.
+            // (The empty asm keeps this address arithmetic inside the
+            // branch: hoisted, every full tile paid for it.)
+            int over = kbase - klast;
+            asm volatile("" : "+s"(over));
 #pragma unroll
             for (int i = 0; i < ROUNDS; ++i) {
                 const int r = ((wave + NW * i) * 64 + lane) / C::SLOTS;
-                const int excess = max(0, kbase + r - klast);
+                const int excess = max(0, over + r);
                 lds_copy16(base, off[i] - (uint32_t)(excess * D * 2), dst + (wave + NW * i) * 512);
             }
         }
