@@ -359,8 +359,10 @@ int fa_bwd_ex(const void *q, const void *k, const void *v, const void *o,
               const uint8_t *block_mask, hipStream_t stream, int dtype,
               void *workspace, size_t workspace_bytes);
 
-/* Workspace bytes fa_bwd_ex uses for this shape (0: none is used, or the
- * shape is invalid).  Independent of dtype and masks. */
+/* Workspace bytes fa_bwd_ex may use for this shape (0: none is used, or the
+ * shape is invalid).  Independent of dtype and masks: it covers the causal
+ * mask, which splits some grids that are not split without it (a call
+ * without the causal mask then uses part of the workspace, or none). */
 size_t fa_bwd_workspace_size(int B, int H, int H_kv, int N, int d);
 
 /* Query rows (Br) and key rows (Bc) per tile that fa_fwd_ex would use for

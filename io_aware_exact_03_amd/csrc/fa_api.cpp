@@ -315,8 +315,8 @@ int backward(const void *q, const void *k, const void *v, const void *o, const v
     a.nkb = (N + 127) / 128;
     a.scale = scale;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    a.nsplit = split ? fa::bwd_split(B, H, Hkv, N) : 1;
-    a.nsplit_q = split ? fa::bwd_split_q(B, H, N) : 1;
+    a.nsplit = split ? fa::bwd_split(B, H, Hkv, N, causal != 0) : 1;
+    a.nsplit_q = split ? fa::bwd_split_q(B, H, N, causal != 0) : 1;
     a.part = split && a.nsplit > 1 ? static_cast<float *>(workspace) : nullptr;
     a.part_q = nullptr;
     if (split && a.nsplit_q > 1) {

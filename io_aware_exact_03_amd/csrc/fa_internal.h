@@ -83,8 +83,8 @@ struct BwdArgs {
 
 // Splits the backward uses for a shape when given a workspace (dK/dV and
 // dQ), and the workspace bytes they then need (0 when no split is worth it).
-int bwd_split(int B, int H, int Hkv, int N);
-int bwd_split_q(int B, int H, int N);
+int bwd_split(int B, int H, int Hkv, int N, bool causal);
+int bwd_split_q(int B, int H, int N, bool causal);
 uint64_t bwd_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 // Enqueues the backward kernels on `stream`.

@@ -185,8 +185,14 @@ def test_bwd_workspace_size():
     size = fa.fa_bwd_workspace_size
     # grids with at least 512 workgroups are not split
     assert size(1, 16, 16, 16384, 128) == 0 and size(8, 12, 12, 1024, 64) == 0
-    # four key/value heads at 16K already give 512 dK/dV workgroups
-    assert size(1, 16, 4, 16384, 128) == 0
+    # four key/value heads at 16K give 512 dK/dV workgroups of very unequal
+    # causal work: two key-range splits (the causal case sets the size); the
+    # dQ grid (16 x 128 tiles) needs none
+    assert size(1, 16, 4, 16384, 128) == 2 * 2 * 4 * 16384 * 128 * 4
+    # four heads at 16K: 512 dK/dV and 512 dQ workgroups, two splits each
+    assert size(1, 4, 4, 16384, 128) == 2 * 2 * 4 * 16384 * 128 * 4 + 2 * 4 * 16384 * 128 * 4
+    # 512 workgroups of short heads (32 key blocks): no split
+    assert size(2, 8, 8, 4096, 128) == 0
     # multi-query 16K: 128 dK/dV workgroups -> 8 splits x (dK, dV) x N x d
     # floats; the dQ grid (16 x 128 tiles) needs none
     assert size(1, 16, 1, 16384, 128) == 8 * 2 * 16384 * 128 * 4

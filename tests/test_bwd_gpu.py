@@ -305,6 +305,42 @@ def test_gqa_full_size_sampled():
 
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_long_causal_one_round_split(d):
+    """B1 H8 N8192 causal: 512 dK/dV and 512 dQ workgroups of very unequal
+    work (64 key blocks per head), which the workspace splits in two; dQ on
+    sampled rows, dK and dV on sampled keys of two heads, against the FP64
+    oracle, and the same gradients from the unsplit call within the bar."""
+    B, H, N = 1, 8, 8192
+    assert fa.fa_bwd_workspace_size(B, H, H, N, d) == 2 * 2 * B * H * N * d * 4 + 2 * B * H * N * d * 4
+    rng = np.random.Generator(np.random.PCG64(3200 + d))
+    q, k, v, rng = random_qkv(B, H, N, d, 0, "bf16", rng=rng)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    tdo = dev(rng.standard_normal(q.shape, dtype=np.float32))
+    o, lse = fa.fwd(tq, tk, tv, causal=True, scale=scale)
+    dq, dk, dv = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True, scale=scale, workspace=True)
+    dq1, dk1, dv1 = fa.bwd(tq, tk, tv, o, tdo, lse, causal=True, scale=scale, workspace=None)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, N - 1, B * H * N - 1], rng.choice(B * H * N, size=96, replace=False)]))
+    cols = np.concatenate([x * N + np.unique(np.concatenate([[0, N - 1], rng.choice(N, 24, replace=False)]))
+                           for x in (0, B * H - 1)])
+    dout = tdo.float().cpu().numpy()
+    ref = {"dq": oracle.attention_bwd_rows_f64(q, k, v, dout, rows, scale, True)}
+    ref["dk"], ref["dv"] = oracle.attention_bwd_cols_f64(q, k, v, dout, cols, scale, True)
+    rows_t, cols_t = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    got = {"dq": dq.reshape(-1, d)[rows_t], "dk": dk.reshape(-1, d)[cols_t], "dv": dv.reshape(-1, d)[cols_t]}
+    for name, r in ref.items():
+        g = got[name].double().cpu().numpy()
+        err = float(np.abs(g - r).max())
+        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        assert err <= bound, f"{name}: max|dg| = {err:.3e} > {bound:.3e}"
+    for name, a, b in (("dq", dq, dq1), ("dk", dk, dk1), ("dv", dv, dv1)):
+        diff = float((a.float() - b.float()).abs().max())
+        bound = 2 * TOL_REL * max(1.0, float(b.float().abs().max()))
+        assert np.isfinite(diff) and diff <= bound, f"{name}: split vs unsplit {diff:.3e}"
+
+
 def test_mqa_block_sparse_full_size_sampled():
     # Multi-query attention at the block-sparse shape (B4 H16 N4096 d64, one
     # key/value head, the band + global mask): the backward splits each key
