@@ -221,13 +221,16 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
               hipStream_t stream, int dtype, void *workspace,
               size_t workspace_bytes);
 
-/* Workspace bytes fa_fwd_ws uses for this shape and dtype (0: none is used,
- * or the arguments are invalid).  Independent of H_kv, masks and scale. */
+/* Workspace bytes fa_fwd_ws may use for this shape and dtype (0: none is
+ * used, or the arguments are invalid).  Independent of H_kv, masks and
+ * scale: it covers the causal mask, which splits some grids that are not
+ * split without it (a call without the causal mask then uses part of the
+ * workspace, or none). */
 size_t fa_fwd_workspace_size(int B, int H, int N, int d, int dtype);
 
 /* Size of the library's static scratch (fa_fwd_noalloc): the largest
  * workspace fa_fwd_workspace_size returns for any shape.  A split is only
- * used on grids of fewer than 512 query tiles, with at most 1024 shares in
+ * used on grids of at most 512 query tiles, with at most 1024 shares in
  * all, so its partials cover at most 1024 * 128 rows of d + 1 <= 129 floats. */
 #define FA_NOALLOC_SCRATCH_BYTES ((size_t)1024 * 128 * 129 * 4)
 

@@ -157,9 +157,10 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     // shape gains from it; bf16/fp16 with the tuned tile only.  With the
     // static scratch (fa_fwd_noalloc) the workspace is the library's own
     // array, looked up only now that every argument has been checked.
-    const uint64_t need = fa::fwd_workspace_bytes(B, H, N, d);
     const bool splittable = dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
-    if (static_scratch && need > 0 && splittable) {
+    const int nsplit = splittable ? fa::fwd_split(B, H, N, causal != 0) : 1;
+    const uint64_t need = fa::fwd_split_bytes(B, H, N, d, nsplit);
+    if (static_scratch && need > 0) {
         if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_INVALID_SHAPE;
         hipError_t e = hipSuccess;
         const uintptr_t p = scratch_on_current_device(&e);
@@ -170,7 +171,7 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
         workspace = reinterpret_cast<void *>(p);
         workspace_bytes = FA_NOALLOC_SCRATCH_BYTES;
     }
-    const bool split = workspace && need > 0 && splittable;
+    const bool split = workspace && need > 0;
     if (split) {
         if (workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
         if (overlaps(workspace, need, q, bytes) || overlaps(workspace, need, k, kv_bytes) ||
@@ -195,7 +196,7 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     a.nkb = (N + 127) / 128;
     a.order = order;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    a.nsplit = split ? fa::fwd_split(B, H, N) : 1;
+    a.nsplit = split ? nsplit : 1;
     const uint64_t rows = (uint64_t)B * H * N;
     a.part_o = split ? static_cast<float *>(workspace) : nullptr;
     a.part_l = split ? static_cast<float *>(workspace) + (uint64_t)a.nsplit * rows * d : nullptr;

@@ -649,21 +649,31 @@ const Instance *f16_tuned_instances() {
 // small for the 256 CUs and a causal grid's longest tile dominates: if it
 // has fewer than 512 workgroups, the largest power of two (at most 16) that
 // keeps it within 1024.  (Measured on B1 H2 N16384: 4 shares 172 us,
-// 8 shares 181 us, 16 shares 246 us, unsplit 299 us; a grid of 512 gained
-// nothing.)
-int fwd_split(int B, int H, int N) {
+// 8 shares 181 us, 16 shares 246 us, unsplit 299 us.)  A causal grid of
+// exactly 512 tiles with long heads (64 or more query tiles) is split in two
+// as well: one round pairs its heaviest and lightest tiles on the same CUs
+// (same box, alternating runs: B1 H4 N16384 d128 338 -> 312 us, B2 H2
+// N16384 320 -> 294 us, B1 H8 N8192 168 -> 162 us; at d = 64 B1 H8 N8192
+// 119 -> 99 us, B1 H4 N16384 227 -> 179 us), while a non-causal one ran 4 %
+// slower split.  Shares stay within 1024, the size of the static scratch.
+int fwd_split(int B, int H, int N, bool causal) {
     if (B < 1 || H < 1 || N < 1) return 1;
-    const int64_t base = (int64_t)B * H * ((N + 127) / 128);
-    if (base >= 512) return 1;
+    const int nqt = (N + 127) / 128;
+    const int64_t base = (int64_t)B * H * nqt;
+    if (base > 512 || (base == 512 && !(causal && nqt >= 64))) return 1;
     int s = 1;
     while (s < 16 && base * s * 2 <= 1024) s *= 2;
     return s;
 }
 
-uint64_t fwd_workspace_bytes(int B, int H, int N, int d) {
-    const int s = fwd_split(B, H, N);
-    if (s == 1) return 0;
+uint64_t fwd_split_bytes(int B, int H, int N, int d, int s) {
+    if (s <= 1) return 0;
     return (uint64_t)s * B * H * (uint64_t)N * (d + 1) * sizeof(float);
+}
+
+uint64_t fwd_workspace_bytes(int B, int H, int N, int d) {
+    // the causal case splits at least as much as any other
+    return fwd_split_bytes(B, H, N, d, fwd_split(B, H, N, true));
 }
 
 hipError_t launch_fwd_split(const FwdArgs &a, int d, int causal, int f16, hipStream_t stream) {

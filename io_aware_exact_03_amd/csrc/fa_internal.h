@@ -34,7 +34,8 @@ struct FwdArgs {
 
 // Key-range split the forward uses for a shape when given a workspace, and
 // the workspace bytes it then needs (0 when no split is worth it).
-int fwd_split(int B, int H, int N);
+int fwd_split(int B, int H, int N, bool causal);
+uint64_t fwd_split_bytes(int B, int H, int N, int d, int nsplit);
 uint64_t fwd_workspace_bytes(int B, int H, int N, int d);
 
 // Enqueues the split forward (tuned kernel with key ranges, then the merge)

@@ -259,6 +259,11 @@ def test_fwd_workspace_size():
     # 300 tiles -> 2 shares (600 <= 1024 < 1200); 1 tile -> 16 shares (the cap)
     assert size(3, 1, 12800, 64, fa.DTYPE_BF16) == 2 * 3 * 12800 * 65 * 4
     assert size(1, 1, 100, 64, fa.DTYPE_BF16) == 16 * 100 * 65 * 4
+    # exactly 512 tiles of long heads (64+ tiles each): two shares, which the
+    # causal mask uses (the size covers it); short heads stay unsplit
+    assert size(1, 4, 16384, 128, fa.DTYPE_BF16) == 2 * 4 * 16384 * (128 + 1) * 4
+    assert size(2, 2, 16384, 64, fa.DTYPE_BF16) == 2 * 4 * 16384 * (64 + 1) * 4
+    assert size(4, 16, 1024, 64, fa.DTYPE_BF16) == 0
     # fp32 is never split; invalid arguments report 0
     assert size(1, 2, 16384, 128, fa.DTYPE_F32) == 0
     assert size(0, 2, 100, 64, 0) == 0 and size(1, 2, 100, 96, 0) == 0
@@ -284,7 +289,7 @@ def test_fwd_workspace_validation(ws, nbytes, status):
 
 def test_noalloc_scratch_covers_every_split_workspace():
     """The static scratch of fa_fwd_noalloc is the largest workspace the
-    key-range split asks for: splits run only on grids of fewer than 512
+    key-range split asks for: splits run only on grids of at most 512
     query tiles of 128 rows, with at most 1024 shares in all."""
     text = open(HEADER).read()
     m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) \* (\d+) \* (\d+) \* (\d+)\)", text)

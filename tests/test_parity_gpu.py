@@ -735,11 +735,14 @@ def test_split_forward_f16_and_gqa(d):
     check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, TOL_BF16, "split gqa")
 
 
-@pytest.mark.parametrize("H,N,d,causal", [(2, 16384, 128, True), (1, 32768, 128, True), (2, 16384, 64, False)])
+@pytest.mark.parametrize("H,N,d,causal", [(2, 16384, 128, True), (1, 32768, 128, True), (2, 16384, 64, False),
+                                           (4, 16384, 128, True), (4, 16384, 64, True), (4, 16384, 128, False)])
 def test_split_forward_one_gpu_share_sampled_rows(H, N, d, causal):
     """The one-GPU share of a head-sharded 16K problem, and a single 32K
     head, at full size: sampled rows against the oracle, all rows finite,
-    and the whole output within the bar of the unsplit kernel's."""
+    and the whole output within the bar of the unsplit kernel's.  H = 4 is
+    a grid of exactly 512 query tiles: split in two with the causal mask,
+    unsplit without it (the workspace is then unused)."""
     inp = custom(1, H, N, d, seed=105 + H, causal=causal, amp=0.5)
     need = fa.fa_fwd_workspace_size(1, H, N, d, fa.DTYPE_BF16)
     assert need > 0

@@ -73,6 +73,7 @@ CASES = [
     (2, 1, 3000, 64, "bf16", False, [3000, 1700], True),
     (1, 3, 1000, 128, "f16", True, None, False),
     (4, 16, 1024, 64, "bf16", True, None, False),  # 512 query tiles: no split, no scratch
+    (1, 4, 16384, 128, "bf16", True, None, False),  # 512 tiles of long causal heads: two shares, the whole scratch
 ]
 
 
