@@ -65,6 +65,15 @@ __device__ __forceinline__ bool wave_any(bool pred) {
     return __builtin_amdgcn_ballot_w64(pred) != 0;
 }
 
+// Issue priority of the calling wave (s_setprio takes an immediate).  The
+// SIMD picks the highest-priority ready wave, the oldest among equals.
+__device__ __forceinline__ void set_wave_priority(int level) {
+    if (level >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (level == 2) __builtin_amdgcn_s_setprio(2);
+    else if (level == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // Key/value head read by query head bh = b*H + h: consecutive groups of
 // H/Hkv query heads share one key/value head (grouped-query attention;
 // Hkv = H is plain multi-head attention, Hkv = 1 multi-query attention).
