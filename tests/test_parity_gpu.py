@@ -315,6 +315,29 @@ def test_block_mask_rows_over_several_chunks(d, causal):
               f"d={d} causal={causal} split={ws is not None}")
 
 
+def test_block_mask_rows_past_four_chunks():
+    """A 33024-token head (258 mask blocks per row, five 64-block chunks) at
+    d = 64 without the causal mask: the tuned kernel there counts a row's
+    active blocks over its first four chunks to set the waves' issue
+    priority, so rows whose only active blocks lie past block 255 (and rows
+    with none) must still be computed in full; sampled rows of every row
+    kind, direct and with the key-range split."""
+    N, d = 33024, 64
+    nb = N // 128
+    inp = custom(1, 1, N, d, seed=97, causal=False, amp=0.5, block_mask=_multi_chunk_mask(nb))
+    assert inp["block_mask"].reshape(nb, nb)[0, :256].sum() == 0
+    blocks = [0, 1, 2, 3, 4, 63, 64, 127, 128, 191, 192, 255, 256, 257]
+    rows = np.array(sorted({min(N - 1, r * 128 + o) for r in blocks for o in (0, 127)}), dtype=np.int64)
+    o_ref, lse_ref = oracle.attention_rows_f64(inp["q"], inp["k"], inp["v"], rows, float(inp["scale"]), False,
+                                               None, inp["block_mask"], 128)
+    assert np.isinf(lse_ref).any() and np.isfinite(lse_ref).any()
+    need = fa.fa_fwd_workspace_size(1, 1, N, d, fa.DTYPE_BF16)
+    for ws in (None, garbage_workspace(need)):
+        o, lse = run(inp, workspace=ws)
+        check(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, TOL_BF16,
+              f"N={N} split={ws is not None}")
+
+
 @pytest.mark.parametrize("H,N,Br", [(2, 4096, 0), (1, 4096, 0), (4, 4096, 64), (2, 4096, 32)])
 def test_heads_spanning_several_xcds(H, N, Br):
     """Few heads: one head's query tiles are shared round-robin by several
