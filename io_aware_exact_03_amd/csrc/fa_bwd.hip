@@ -181,10 +181,14 @@ __global__ __launch_bounds__(256) void bwd_delta(BwdArgs a) {
 // run in ascending order.  Causal grids, where key block kt is seen by the
 // query rows from kt on (the first blocks the most), use the CU-balanced
 // order of xcd_item_causal instead (heaviest blocks of every head first).
+// With per-batch key lengths (the key blocks past a batch entry's length
+// carry no work) whole key/value heads are dealt to the XCDs round-robin
+// (xcd_item_units), so every XCD gets the same share of every entry.
 __device__ __forceinline__ void dkdv_block(int nkt, int nsplit, int *split, int *bkv, int *kt, bool causal,
-                                           int resident) {
+                                           int resident, bool by_units) {
     // resident: workgroups of the kernel that fit one CU together
-    int id = causal ? xcd_item_causal(nkt * nsplit, resident) : xcd_item(nkt * nsplit);
+    int id = causal ? xcd_item_causal(nkt * nsplit, resident)
+                    : (by_units ? xcd_item_units(nkt * nsplit, nkt * nsplit) : xcd_item(nkt * nsplit));
     *split = id % nsplit;
     id /= nsplit;
     *bkv = id / nkt;
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv(BwdArgs a) {
     // Workgroup -> (batch, key/value head, key block, query-head split);
     // causal grids start with the key blocks that see the most query rows.
     int split, bkv, kt;
-    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL, 2);
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL, 2, a.key_len != nullptr);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + wave * 32;
@@ -484,7 +488,7 @@ __global__ __launch_bounds__(512, D == 64 ? 2 : 1) void bwd_dkdv_pair(BwdArgs a)
     const int N = a.N;
     const int nkt = (N + BK - 1) / BK;
     int split, bkv, kt;
-    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL, 1);
+    dkdv_block(nkt, a.nsplit, &split, &bkv, &kt, CAUSAL, 1, a.key_len != nullptr);
     const int b = bkv / a.Hkv;
     const int hkv = bkv - b * a.Hkv;
     const int k0 = kt * BK, kw0 = k0 + kg * 32;
@@ -720,9 +724,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq(BwdArgs a) {
     const int nqt = (N + BR - 1) / BR;
     // (query tile, key-range split): the splits of one query tile adjacent,
     // heads and tiles in the XCD-aware order; causal grids longest first in
-    // the CU-balanced order.
-    // two (d = 128) or three (d = 64) workgroups per CU
-    const int item = CAUSAL ? xcd_item_causal(nqt * a.nsplit_q, D == 128 ? 2 : 3) : xcd_item(nqt * a.nsplit_q);
+    // the CU-balanced order (two (d = 128) or three (d = 64) workgroups per
+    // CU); with per-batch key lengths the query heads of one key/value head
+    // are dealt to the XCDs round-robin (xcd_item_units).
+    const int per_head = nqt * a.nsplit_q;
+    const int item = CAUSAL ? xcd_item_causal(per_head, D == 128 ? 2 : 3)
+                            : (a.key_len ? xcd_item_units(a.group * per_head, per_head) : xcd_item(per_head));
     const int split = item % a.nsplit_q;
     const int rest = item / a.nsplit_q;
     const int bh = rest / nqt;

@@ -105,6 +105,28 @@ __device__ __forceinline__ int xcd_item(int per_head) {
     return x * per + local;
 }
 
+// Work item of this workgroup on a grid whose items differ by batch entry
+// (per-batch key lengths) but not within a head.  The contiguous shares of
+// xcd_item would give each XCD a few whole batch entries, and the XCD with
+// the longest ones would set the time.  Here units of `unit` consecutive
+// items (the query heads that share one key/value head, all their tiles)
+// go to the XCDs round-robin: XCD x takes units x, x + 8, x + 16, ..., so
+// every XCD gets the same slice of every batch entry, and the CUs of an XCD
+// (which take its workgroups l, l + 32, ...; see xcd_item_causal) get units
+// of different entries.  A unit stays on one XCD, so its K/V re-reads stay
+// in one L2.  Falls back to xcd_item when the shares do not hold whole
+// units.
+__device__ __forceinline__ int xcd_item_units(int unit, int per_head) {
+    const int G = gridDim.x;
+    const int id = blockIdx.x;
+    if ((G & 7) != 0) return id;
+    const int per = G >> 3;
+    if (unit < 1 || per % unit != 0) return xcd_item(per_head);
+    const int x = id & 7, local = id >> 3;
+    const int k = local / unit;
+    return (x + 8 * k) * unit + (local - k * unit);
+}
+
 // Work item of this workgroup on a causal grid, where the items of a head
 // differ in cost (query tile qt sees the keys of query tiles 0..qt).  The
 // XCD shares are those of xcd_item; within a share the order changes so
@@ -163,10 +185,13 @@ __device__ __forceinline__ int xcd_item_causal(int per_head, int resident) {
 // Workgroup -> (head, query tile).  Causal grids take the longest query
 // tiles first, in the CU-balanced order of xcd_item_causal; other grids
 // take each head's tiles in order, whole heads per XCD where possible
-// (keeping a head's K/V re-reads inside one XCD's L2).
+// (keeping a head's K/V re-reads inside one XCD's L2), and with
+// unit > 0 (per-batch key lengths) units of that many items dealt to the
+// XCDs round-robin (xcd_item_units).
 __device__ __forceinline__ void tile_of_block(int nqt, bool longest_first, int resident,
-                                              int *bh, int *qt) {
-    const int id = longest_first ? xcd_item_causal(nqt, resident) : xcd_item(nqt);
+                                              int *bh, int *qt, int unit = 0) {
+    const int id = longest_first ? xcd_item_causal(nqt, resident)
+                                 : (unit > 0 ? xcd_item_units(unit, nqt) : xcd_item(nqt));
     *bh = id / nqt;
     const int r = id - *bh * nqt;
     *qt = longest_first ? nqt - 1 - r : r;

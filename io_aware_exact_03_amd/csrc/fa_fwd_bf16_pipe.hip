@@ -148,7 +148,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_pipe(FwdArgs a) 
     } else {
         // workgroups resident per CU: 2 at d = 128 and 3 at d = 64 with 4
         // waves (238 and 168 registers), 1 with 8 waves
-        tile_of_block(nqt, CAUSAL, NW == 4 ? (D == 128 ? 2 : 3) : 1, &bh, &qt);
+        tile_of_block(nqt, CAUSAL, NW == 4 ? (D == 128 ? 2 : 3) : 1, &bh, &qt,
+                      !CAUSAL && a.key_len ? a.group * nqt : 0);
     }
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_flat(FwdArgs a) {
     const int N = a.N;
     const int nqt = (N + BR - 1) / BR;
     int bh, qt;
-    tile_of_block(nqt, CAUSAL, OCC, &bh, &qt);
+    tile_of_block(nqt, CAUSAL, OCC, &bh, &qt, !CAUSAL && a.key_len ? a.group * nqt : 0);
     const int b = bh / a.H;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t kvhead = (int64_t)kv_head_of(bh, a) * N * D;
