@@ -131,6 +131,16 @@ def test_bwd_two_per_cu_split(causal, H, H_kv):
     run_case(4, H, H_kv, 1000, 128, seed=402, causal=causal, workspace=True)
 
 
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(8, 8, 2, 512, 128), (16, 4, 4, 512, 64), (8, 16, 16, 512, 64)])
+def test_bwd_key_padded_unit_order(B, H, H_kv, N, d):
+    """Key-padded grids whose per-XCD shares hold whole key/value-head units,
+    so the dK/dV and dQ kernels deal the units to the XCDs round-robin;
+    ragged key lengths with an entry that has no key; gradients start as
+    NaN."""
+    rng = np.random.default_rng(410 + B + H + d)
+    run_case(B, H, H_kv, N, d, seed=411 + d, key_len=key_lengths(B, N, rng))
+
+
 def test_bwd_two_per_cu_f16():
     run_case(13, 16, 16, 520, 128, seed=403, causal=True, dtype="f16")
 

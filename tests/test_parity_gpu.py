@@ -635,6 +635,22 @@ def test_gqa_bf16(H, H_kv, d, mode):
     check(o, lse, *ref(inp), TOL_BF16, f"gqa H={H} H_kv={H_kv} d={d} {mode}")
 
 
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(8, 8, 2, 512, 128), (16, 4, 4, 512, 64), (8, 16, 16, 640, 64),
+                                         (16, 16, 16, 512, 128)])
+def test_key_padded_unit_order(B, H, H_kv, N, d):
+    """Key-padded grids whose per-XCD shares hold whole key/value-head units,
+    so the tuned kernels deal the units to the XCDs round-robin (grouped
+    heads, a ragged N, both head sizes); ragged key lengths with an entry
+    that has no key and one that has all; every output against the
+    oracle."""
+    rng = np.random.default_rng(420 + B + H + d)
+    kl = rng.integers(1, N + 1, B)
+    kl[0], kl[-1] = 0, N
+    inp = gqa_custom(B, H, H_kv, N, d, seed=421 + d, key_len=kl)
+    o, lse = run(inp)
+    check(o, lse, *ref(inp), TOL_BF16, f"B={B} H={H} H_kv={H_kv} N={N} d={d}")
+
+
 @pytest.mark.parametrize("Br,Bc", [(64, 32), (16, 128)])
 def test_gqa_tile_study_kernels(Br, Bc):
     inp = gqa_custom(1, 6, 3, 200, 128, seed=42, causal=True)
