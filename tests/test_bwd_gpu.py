@@ -251,6 +251,36 @@ def test_bwd_full_size_sampled(workload):
         assert err <= bound, f"{workload} {name}: max|dg| = {err:.3e} > {bound:.3e}"
 
 
+@pytest.mark.parametrize("workload", ["gpt2_causal", "bert_padded", "block_sparse", "long_causal"])
+def test_bwd_full_size_every_element(workload):
+    # The whole workload at its full size, in the launch configuration the
+    # backward report times, compared element by element with the full FP64
+    # backward oracle: every element of dQ, dK and dV.  (The oracle holds an
+    # N x N array of doubles per head; the 16K causal workload costs it
+    # 2-10 s of host time per head.)
+    w = WORKLOADS[workload]
+    inp = make_inputs(w)
+    rng = np.random.default_rng(w.seed + 600)
+    tq, tk, tv = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    tdo = dev(rng.standard_normal(inp["q"].shape, dtype=np.float32))
+    kl = torch.from_numpy(inp["key_len"]).cuda() if inp["key_len"] is not None else None
+    bm = torch.from_numpy(inp["block_mask"]).cuda() if inp["block_mask"] is not None else None
+    scale = float(inp["scale"])
+    o, lse = fa.fwd(tq, tk, tv, causal=w.causal, key_len=kl, block_mask=bm, scale=scale)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (tq, tk, tv))
+    fa.bwd(tq, tk, tv, o, tdo, lse, causal=w.causal, key_len=kl, block_mask=bm, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd_f64(inp["q"], inp["k"], inp["v"], tdo.float().cpu().numpy(), scale, w.causal,
+                                   inp["key_len"], inp["block_mask"])
+    for name, g, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        g = g.double().cpu().numpy()
+        assert np.all(np.isfinite(g)), f"{workload} {name}: non-finite"
+        err = float(np.abs(g - r).max())
+        bound = TOL_REL * max(1.0, float(np.abs(r).max()))
+        print(f"{workload} {name}: {g.size} elements, max|dg| = {err:.3e} (bar {bound:.3e})", flush=True)
+        assert err <= bound, f"{workload} {name}: max|dg| = {err:.3e} > {bound:.3e}"
+
+
 def test_bwd_larger_causal():
     run_case(1, 2, 2, 1000, 128, seed=73, causal=True)
 

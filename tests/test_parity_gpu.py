@@ -181,18 +181,24 @@ def test_large_workloads_sampled_rows(name):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("name", ["long_causal", "block_sparse"])
-def test_large_workloads_full(name):
+def test_large_workloads_full(name, dtype):
     """Every row of O and LSE of the two long workloads (16K causal d = 128;
     4K block-sparse d = 64 with its seeded mask) against the full FP64
-    oracle, on the same launch configuration the benchmark times."""
+    oracle, on the same launch configuration the benchmark times; in bf16
+    (the workloads' type) and with the same draws rounded to fp16 instead
+    (the tuned kernel's fp16 instances, fp16 bar)."""
     w = WORKLOADS[name]
     inp = make_inputs(w)
-    o, lse = run(inp)
+    if dtype == "f16":
+        for n in ("q", "k", "v"):
+            inp[n] = f16_round(inp[n])
+    o, lse = run(inp, dtype=dtype)
     o_ref, lse_ref = ref(inp)
-    err = check(o, lse, o_ref, lse_ref, TOL_BF16, name)
+    err = check(o, lse, o_ref, lse_ref, TOL_BF16 if dtype == "bf16" else TOL_F16, f"{name} {dtype}")
     fin = np.isfinite(lse_ref)
-    print(f"{name}: full comparison over {o.size} outputs: max|dO| = {err:.3e}, "
+    print(f"{name} {dtype}: full comparison over {o.size} outputs: max|dO| = {err:.3e}, "
           f"max|dLSE| = {np.abs(lse[fin] - lse_ref[fin]).max():.3e}", flush=True)
     assert fin.all(), "every row of these workloads sees at least one key"
 
